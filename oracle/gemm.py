@@ -1,0 +1,130 @@
+"""Grouped GEMMs on MXFP8 operands (CPU oracle).
+
+TEST INFRASTRUCTURE ONLY: used by tests, the smoke check and the CPU
+baseline of the benchmark; never by the product path.
+
+Each grouped GEMM is a loop over experts of one float64 matmul of
+dequantized operands; every product of two MXFP8 values is exact in
+float64.  The operand roles follow the pages:
+
+* forward (layout NT, C = A B^T): Y_g = X_g W_g^T from the row-wise X and
+  the row-wise W ("For forward, we directly pass the row-wise quantized
+  for forward grouped gemm", Description of "[Pytorch] Add support for
+  row-wise quanted input for grouped gemm", PR #3244; the forward GEMMs
+  read only the row-wise weight, last commit message of "[PyTorch] Fix
+  distributed BF16 weights and trim NVFP4 saved state in the fused grouped
+  MLP", PR #3545).
+* dgrad (layout NN, C = A B): dX_g = dY_g W_g from the row-wise dY and the
+  column-wise W copy (PR #3244 Description, backward paragraph; PR #3545
+  last commit message: the column-wise weight exists for the dgrad GEMM).
+* wgrad (layout TN, C = A^T B): dW_g = dY_g^T X_g from the column-wise
+  copies of dY and X, contracted over the group's rows (PR #3244 flowchart
+  node "Wgrad grouped GEMM" fed by the column-wise requantize; PR #3545
+  Description: every wgrad path takes the column-wise tiles).
+* The single grouped weight is one [G, N, K] tensor whose out_features is
+  size(-2) ("Improve device-init grouped linear module with single grouped
+  weight support", PR #3224, Greptile Summary, file table); a grouped GEMM
+  equals the per-expert GEMMs (same page: numerical equivalence of single
+  vs discrete parameter layouts).
+
+Physical operand layouts (the same buffers the HIP library takes):
+* X rowwise: codes [T, K], scales [T, K/32].
+* W rowwise: codes [G, N, K], scales [G, N, K/32].
+* W column-wise copy: the transposed copy of W viewed as [G*N, K]:
+  codes [K, G*N], scales [K, G*N/32]; expert g is columns [g*N, (g+1)*N).
+* dY rowwise: codes [T, N], scales [T, N/32].
+* dY / X column-wise copies: codes [N, T] / [K, T], scales [.., T/32].
+"""
+
+import numpy as np
+
+from . import mxfp8
+
+
+def _splits(m_splits, total):
+    m = mxfp8.check_splits(m_splits, total)
+    offs = np.concatenate([[0], np.cumsum(m)]).astype(np.int64)
+    return m, offs
+
+
+def fprop(xq, xs, wq, ws, m_splits, magnitude=False):
+    """Y[rows of g] = X_g W_g^T.  Returns float64 [T, N] (and |X||W|^T)."""
+    xh = mxfp8.dequantize_rowwise(xq, xs)
+    g_count, n, k = wq.shape
+    wh = mxfp8.dequantize_rowwise(wq.reshape(g_count * n, k),
+                                  ws.reshape(g_count * n, k // 32)).reshape(g_count, n, k)
+    t = xh.shape[0]
+    m, offs = _splits(m_splits, t)
+    assert len(m) == g_count
+    out = np.zeros((t, n))
+    mag = np.zeros((t, n)) if magnitude else None
+    for g in range(g_count):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 > r0:
+            out[r0:r1] = xh[r0:r1] @ wh[g].T
+            if magnitude:
+                mag[r0:r1] = np.abs(xh[r0:r1]) @ np.abs(wh[g]).T
+    return (out, mag) if magnitude else out
+
+
+def dgrad(dyq, dys, wcq, wcs, m_splits, num_groups, magnitude=False):
+    """dX[rows of g] = dY_g W_g, with W_g read from the column-wise copy.
+
+    wcq: [K, G*N]; the logical W_g [N, K] is wcq[:, g*N:(g+1)*N]^T.
+    Returns float64 [T, K] (and |dY||W|).
+    """
+    dyh = mxfp8.dequantize_rowwise(dyq, dys)
+    t, n = dyh.shape
+    wct = mxfp8.dequantize_lastdim(wcq, wcs)           # [K, G*N]
+    k = wct.shape[0]
+    assert wct.shape[1] == num_groups * n
+    m, offs = _splits(m_splits, t)
+    assert len(m) == num_groups
+    out = np.zeros((t, k))
+    mag = np.zeros((t, k)) if magnitude else None
+    for g in range(num_groups):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 > r0:
+            w_g = wct[:, g * n:(g + 1) * n].T                 # [N, K]
+            out[r0:r1] = dyh[r0:r1] @ w_g
+            if magnitude:
+                mag[r0:r1] = np.abs(dyh[r0:r1]) @ np.abs(w_g)
+    return (out, mag) if magnitude else out
+
+
+def wgrad(dycq, dycs, xcq, xcs, m_splits, magnitude=False):
+    """dW_g = dY_g^T X_g over the group's rows, from the column-wise copies.
+
+    dycq: [N, T], xcq: [K, T].  Returns float64 [G, N, K] (and magnitudes);
+    an expert with no rows gets dW_g = 0.
+    """
+    a = mxfp8.dequantize_lastdim(dycq, dycs)            # [N, T]
+    b = mxfp8.dequantize_lastdim(xcq, xcs)              # [K, T]
+    n, t = a.shape
+    k = b.shape[0]
+    m, offs = _splits(m_splits, t)
+    out = np.zeros((len(m), n, k))
+    mag = np.zeros((len(m), n, k)) if magnitude else None
+    for g in range(len(m)):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 > r0:
+            out[g] = a[:, r0:r1] @ b[:, r0:r1].T
+            if magnitude:
+                mag[g] = np.abs(a[:, r0:r1]) @ np.abs(b[:, r0:r1]).T
+    return (out, mag) if magnitude else out
+
+
+def tolerance_f32(magnitude):
+    """Allowed |gpu - oracle| for an fp32 output: 1e-5 * sum_k |a_k b_k| + 1e-6.
+
+    Derivation: the kernel accumulates in fp32 (unit roundoff 2^-24 ~ 6e-8);
+    with at most a few hundred sequential fp32 additions of partial sums per
+    output the rounding error stays below 1e-5 of the sum of magnitudes.
+    """
+    return 1e-5 * np.asarray(magnitude, dtype=np.float64) + 1e-6
+
+
+def within_bf16_ulp(gpu_bf16_as_f64, oracle_f64):
+    """True where a bf16 output is within 1 bf16 ulp of the oracle rounded to bf16."""
+    ref = mxfp8.round_to_bf16(oracle_f64)
+    return np.abs(np.asarray(gpu_bf16_as_f64) - ref) <= mxfp8.bf16_ulp(ref)

@@ -1,0 +1,220 @@
+"""Benchmark of the MXFP8 MoE expert grouped-GEMM hot path on one MI355X.
+
+One step = one pass of the whole hot path of an expert linear over one batch:
+  1. row-wise group quantize of X            [T, K]  bf16 -> MXFP8
+  2. row + column-wise quantize of W         [G, N, K] bf16 -> MXFP8 (both copies)
+  3. forward grouped GEMM (NT)               Y  [T, N] = X W_g^T
+  4. column-wise requantize of X             (saved for wgrad)
+  5. row-wise group quantize of dY           [T, N]
+  6. dgrad grouped GEMM (NN)                 dX [T, K] = dY W_g
+  7. column-wise requantize of dY + dbias    dbias [G, N]
+  8. wgrad grouped GEMM (TN)                 dW [G, N, K] = dY_g^T X_g
+Workload: 8 experts, hidden 4096 -> expert FFN 14336 (one linear), 16384
+tokens routed by a seeded Dirichlet(1) multinomial (multiples of 128); X, dY
+~ N(0, 1), W ~ N(0, 0.02) in bf16; fp32 GEMM outputs.  Inputs are resident in
+HBM before the timed region.
+
+value = 3 * 2 T N K / step time (TFLOP/s over the whole step, quantize
+kernels included).  The grouped-GEMM roofline uses the GEMM launches' own
+durations, measured with events on the stream they run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "moe8_h4096_f14336"
+PEAK_MXFP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, 5.0 PFLOP/s
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", default=WORKLOAD)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, budget_rows=1024, n_cols=2048):
+    """Time the CPU oracle on a bounded sample of the same workload.
+
+    Sample: the first `budget_rows` tokens, re-split as 8 experts of 128 rows,
+    the first `n_cols` output features of every expert's weight, the full
+    hidden size; the same eight steps as the GPU step.  Returns TFLOP/s of the
+    three GEMMs over the oracle's whole wall time.
+    """
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import gemm as og
+    from oracle import mxfp8 as om
+
+    g = w.groups
+    rows = budget_rows
+    splits = [rows // g] * g
+    k = w.hidden
+    x = w.tensors["x"][:rows].double().numpy()
+    wt = w.tensors["w"][:, :n_cols, :].double().numpy().reshape(g * n_cols, k)
+    dy = w.tensors["dy"][:rows, :n_cols].double().numpy()
+    t0 = time.perf_counter()
+    xq, xs = om.quantize_rowwise(x)
+    wq, ws = om.quantize_rowwise(wt)
+    wcq, wcs = om.quantize_colwise(wt, [g * n_cols])
+    _y = og.fprop(xq, xs, wq.reshape(g, n_cols, k), ws.reshape(g, n_cols, k // 32), splits)
+    xcq, xcs = om.requant_colwise(xq, xs, splits)
+    dyq, dys = om.quantize_rowwise(dy)
+    _dx = og.dgrad(dyq, dys, wcq, wcs, splits, g)
+    dycq, dycs = om.requant_colwise(dyq, dys, splits)
+    _db = om.grouped_dbias(dyq, dys, splits)
+    _dw = og.wgrad(dycq, dycs, xcq, xcs, splits)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * rows * n_cols * k
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{WORKLOAD}: first {rows} tokens as {g} experts x {rows // g}, "
+                      f"{n_cols} of {w.ffn} output features, K={k}; all 8 steps; "
+                      f"{dt:.2f} s wall, float64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MXFP8 grouped-GEMM "
+              "path here has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.make(args.workload)
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    dev = "cuda"
+    x = w.tensors["x"].to(dev)
+    wt = w.tensors["w"].to(dev)
+    dy = w.tensors["dy"].to(dev)
+    ms = torch.from_numpy(w.m_splits).to(dev)
+    out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+
+    u8 = dict(dtype=torch.uint8, device=dev)
+    xo = mx.MXFP8Tensor(torch.empty(t, k, **u8), torch.empty(t, k // 32, **u8))
+    wo = mx.MXFP8Tensor(torch.empty(g * n, k, **u8), torch.empty(g * n, k // 32, **u8),
+                        torch.empty(k, g * n, **u8), torch.empty(k, g * n // 32, **u8))
+    xc = mx.MXFP8Tensor(col_data=torch.empty(k, t, **u8), col_scale=torch.empty(k, t // 32, **u8))
+    dyo = mx.MXFP8Tensor(torch.empty(t, n, **u8), torch.empty(t, n // 32, **u8))
+    dyc = mx.MXFP8Tensor(col_data=torch.empty(n, t, **u8), col_scale=torch.empty(n, t // 32, **u8))
+    y = torch.empty(t, n, dtype=out_dtype, device=dev)
+    dx = torch.empty(t, k, dtype=out_dtype, device=dev)
+    dw = torch.empty(g, n, k, dtype=out_dtype, device=dev)
+    db = torch.empty(g, n, dtype=torch.float32, device=dev)
+    ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8)
+
+    ev = {}
+
+    def timed(name, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        ev.setdefault(name, []).append((a, b))
+        return r
+
+    def step():
+        timed("quant_x", lambda: mx.group_quantize(x, mx.ROWWISE, out=xo))
+        timed("quant_w", lambda: mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo))
+        timed("gemm_fprop", lambda: mx.grouped_gemm(
+            "NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k, out_dtype, y))
+        timed("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc))
+        timed("quant_dy", lambda: mx.group_quantize(dy, mx.ROWWISE, out=dyo))
+        timed("gemm_dgrad", lambda: mx.grouped_gemm(
+            "NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n, k, out_dtype,
+            dx))
+        timed("requant_dy_dbias", lambda: mx.requant_colwise(
+            dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db, workspace=ws))
+        timed("gemm_wgrad", lambda: mx.grouped_gemm(
+            "TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, out_dtype,
+            dw))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev.clear()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    per = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
+    flop_one = 2.0 * t * n * k
+    gemm_ms = per["gemm_fprop"] + per["gemm_dgrad"] + per["gemm_wgrad"]
+    gemm_tflops = 3 * flop_one / (gemm_ms * 1e-3) / 1e12
+    value = 3 * flop_one / (ms_step * 1e-3) / 1e12
+    # algorithmic HBM bytes of the streaming kernels
+    q_bytes = {
+        "quant_x": t * k * (2 + 1 + 1 / 32),
+        "quant_w": g * n * k * (2 + 2 * (1 + 1 / 32)),
+        "requant_x": t * k * 2 * (1 + 1 / 32),
+        "quant_dy": t * n * (2 + 1 + 1 / 32),
+        "requant_dy_dbias": t * n * 2 * (1 + 1 / 32) + t * n * 4 / 128 * 2 + g * n * 4,
+    }
+    quant_ms = sum(per[nm] for nm in q_bytes)
+    quant_gbs = sum(q_bytes.values()) / (quant_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "MXFP8 grouped GEMM TFLOP/s (fprop+dgrad+wgrad); group-quantize HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3 (fp32 accumulate, fp32 out)" if out_dtype == torch.float32
+                 else "mxfp8-e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "experts": g, "tokens": t, "hidden": k,
+                   "ffn": n, "m_splits": [int(v) for v in w.m_splits],
+                   "out_dtype": w.out_dtype},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "group_quantize_gbs": round(quant_gbs, 1),
+        "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "grouped_gemm_kernel (3 launches per step)"},
+        "quantize_roofline": {"bound": "hbm", "achieved": round(quant_gbs, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(quant_gbs / PEAK_HBM_GBS, 4)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * mxfp8moe.h -- C ABI of the MXFP8 MoE expert grouped-GEMM library (gfx950).
+ *
+ * The hot path of an MoE expert linear layer on MXFP8 data, as described on
+ * the NVIDIA TransformerEngine pull-request pages
+ *   [P3244] "[Pytorch] Add support for row-wise quanted input for grouped gemm"
+ *   [P3545] "[PyTorch] Fix distributed BF16 weights and trim NVFP4 saved state
+ *            in the fused grouped MLP"
+ *   [P3224] "Improve device-init grouped linear module with single grouped
+ *            weight support"
+ * with the MXFP8 arithmetic of the OCP Microscaling Formats (MX) v1.0
+ * specification (sections 5 and 6.3), which the pages leave unstated.
+ *
+ * Formats and conventions used by every entry point
+ * -------------------------------------------------
+ *  - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *  - MXFP8 data bytes are E4M3 ("FN": max 448, no infinity) and scale bytes
+ *    are E8M0 (value 2^(u-127)).  A block of 32 values shares one scale:
+ *      X = floor(log2(max|v|)) - 8, clamped to [-127, 127] (0 for an all-zero
+ *      block, i.e. byte 0); each element is the E4M3 value nearest to v/2^X,
+ *      ties to the even code, saturating at +-448; the sign of zero is kept.
+ *  - Row-wise data of a [R, C] tensor: bytes [R, C] row-major, scales
+ *    [R, C/32] row-major, blocks of 1 x 32 along C ([P3244] Description).
+ *  - Column-wise data of a [R, C] tensor (blocks of 32 x 1 along R) is stored
+ *    transposed: bytes [C, R] and scales [C, R/32], both row-major.  It is the
+ *    copy the wgrad GEMM reads ([P3244] Greptile Summary flowchart;
+ *    [P3545] Description: every wgrad path takes the column-wise tiles).
+ *  - Scale arrays have exactly the shape (T, K/32): the page's padded shape
+ *    (round_up(T,128), round_up(K/32,4)) ([P3244] review thread on
+ *    scale_shape) has no padding under the alignment contract below.
+ *  - Alignment contract ([P3244] review thread on scale_shape: per-expert
+ *    128-token alignment from the dispatch, hidden % 512 == 0, assert rather
+ *    than pad): T % 128 == 0, every m_splits[g] % 128 == 0 and >= 0,
+ *    sum(m_splits) == T, K % 512 == 0, N % 512 == 0.  Host-checkable parts
+ *    are checked (MXFP8_EINVAL); the device-resident splits are checked only
+ *    by mxfp8_validate_splits.  Under this contract column-wise blocks never
+ *    straddle an expert boundary, so the quantize/requant bytes do not depend
+ *    on the split.
+ *  - m_splits is a DEVICE array of int64 ([P3224] review: the native grouped
+ *    path requires CUDA int64 m_splits and errors on host splits).  A host
+ *    pointer is rejected with MXFP8_EINVAL.
+ *  - Every buffer is caller-owned device memory.  Outputs are fully
+ *    overwritten in place (the output= reuse of [P3224] Greptile Summary).
+ *    No entry point allocates, frees or synchronizes; all work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream), so the calls can
+ *    be captured in a HIP graph.  Kernels never fill memory with a memset
+ *    node.
+ *  - Errors: the return value is a status code; mxfp8_last_error() gives a
+ *    message for the last failing call on this thread.  MXFP8_EINVAL mirrors
+ *    the pages' ValueError (bad shapes, NULL pointers, host m_splits),
+ *    MXFP8_ENOTSUP their NotImplementedError (unsupported format requests),
+ *    MXFP8_EHIP their RuntimeError (a HIP launch failure).
+ */
+#ifndef MXFP8MOE_H
+#define MXFP8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxfp8_status {
+  MXFP8_OK = 0,
+  MXFP8_EINVAL = 1,
+  MXFP8_ENOTSUP = 2,
+  MXFP8_EHIP = 3
+} mxfp8_status;
+
+/* GEMM layouts, row-major letters: NT: C = A B^T, NN: C = A B, TN: C = A^T B. */
+typedef enum mxfp8_layout {
+  MXFP8_LAYOUT_NT = 0, /* forward  */
+  MXFP8_LAYOUT_NN = 1, /* dgrad    */
+  MXFP8_LAYOUT_TN = 2  /* wgrad    */
+} mxfp8_layout;
+
+typedef enum mxfp8_out_dtype {
+  MXFP8_OUT_F32 = 0,
+  MXFP8_OUT_BF16 = 1
+} mxfp8_out_dtype;
+
+#define MXFP8_ROWWISE 1u
+#define MXFP8_COLWISE 2u
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* mxfp8_last_error(void);
+
+/* ABI version of this header (incremented on any signature change). */
+int32_t mxfp8_abi_version(void);
+
+/*
+ * mxfp8_group_quantize -- bf16 grouped token tensor -> MXFP8.
+ * Row-wise ([P3244] Description: the grouped GEMM takes input already
+ * quantized row-wise) and/or column-wise ([P3244] review: the column-wise
+ * scales come from the group quantize kernel) in one pass over x.
+ *
+ *   x      [T, K] bf16, row-major (device)
+ *   usage  MXFP8_ROWWISE | MXFP8_COLWISE (at least one)
+ *   q_row  [T, K] u8,  s_row [T, K/32] u8        (required iff ROWWISE)
+ *   q_col  [K, T] u8,  s_col [K, T/32] u8        (required iff COLWISE)
+ * The same call quantizes a grouped weight [G, N, K] viewed as [G*N, K]
+ * (T = G*N); its column-wise copy is then [K, G*N], expert g being columns
+ * [g*N, (g+1)*N).
+ * Errors: EINVAL for NULL required pointers, T % 128, K % 512, usage == 0.
+ */
+mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint32_t usage,
+                                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                  uint8_t* s_col, void* stream);
+
+/*
+ * Bytes of device workspace that mxfp8_requant_colwise (with dbias) and
+ * mxfp8_grouped_dbias need for a [T, N] operand: one fp32 partial sum per
+ * 128-row tile and column, i.e. (T/128) * N * 4.
+ */
+size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N);
+
+/*
+ * mxfp8_requant_colwise -- row-wise MXFP8 -> exact dequantize -> column-wise
+ * MXFP8, optionally with the fused grouped bias gradient
+ * ([P3244] Description: dequant + requant with col-wise to save for
+ * backward / for wgrad; Greptile Summary: dbias reduced directly from the
+ * dequantized gradient).
+ *
+ *   q_row [T, K] u8, s_row [T, K/32] u8     (device)
+ *   q_col [K, T] u8, s_col [K, T/32] u8     (device, written)
+ *   dbias NULL, or [G, K] fp32 (device, written): dbias[g, k] = sum over the
+ *         rows r of expert g of dequant(q_row)[r, k]; 0 for an empty expert.
+ *         Needs m_splits (device int64 [G]) and a workspace of
+ *         mxfp8_dbias_workspace_bytes(T, K) bytes; the sum order is fixed, so
+ *         results are bitwise reproducible.
+ * Errors: EINVAL for NULL pointers, T % 128, K % 512, G < 1, host m_splits,
+ * a workspace smaller than required.
+ */
+mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                   int64_t K, uint8_t* q_col, uint8_t* s_col,
+                                   const int64_t* m_splits, int32_t G, float* dbias,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mxfp8_grouped_dbias -- grouped bias gradient from row-wise MXFP8 dY with no
+ * column-wise copy (the frozen-weight case: [P3244] Greptile Summary, dbias
+ * reduced without a wgrad stage).
+ *   q_row [T, N] u8, s_row [T, N/32] u8; dbias [G, N] fp32 (written).
+ * Same workspace and errors as mxfp8_requant_colwise.
+ */
+mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                 int64_t N, const int64_t* m_splits, int32_t G, float* dbias,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mxfp8_grouped_gemm -- the three grouped GEMMs of an expert linear
+ * y = x W^T (in_features K, out_features N, grouped weight [G, N, K],
+ * [P3224] Greptile Summary) on MXFP8 operands, fp32 accumulation.
+ * Expert g owns token rows [o_g, o_g + m_splits[g]), o_g = sum of the
+ * previous splits.
+ *
+ *  NT (forward, [P3244] Description: row-wise data goes straight to the
+ *      forward grouped GEMM):
+ *      a = X row-wise  [T, K] + [T, K/32]
+ *      b = W row-wise  [G, N, K] + [G, N, K/32]
+ *      c [T, N]:  c[r] = X[r] W_g^T for r in expert g
+ *  NN (dgrad, [P3244] Description backward paragraph; [P3545] last commit
+ *      message: the column-wise weight copy exists for dgrad):
+ *      a = dY row-wise [T, N] + [T, N/32]
+ *      b = W column-wise copy [K, G*N] + [K, G*N/32]
+ *      c [T, K]:  c[r] = dY[r] W_g
+ *  TN (wgrad, [P3244] flowchart: column-wise requantize feeds the wgrad
+ *      grouped GEMM):
+ *      a = dY column-wise copy [N, T] + [N, T/32]
+ *      b = X column-wise copy  [K, T] + [K, T/32]
+ *      c [G, N, K]: c[g] = sum over r in expert g of dY[r]^T X[r];
+ *      an expert with no rows gets c[g] = 0.
+ *  c_dtype: MXFP8_OUT_F32 or MXFP8_OUT_BF16 (round to nearest even).
+ *  Rows of c that belong to no expert (none under the contract) are not
+ *  written by NT/NN.
+ * Errors: EINVAL for NULL pointers, bad layout, T % 128, N % 512, K % 512,
+ * G < 1, host m_splits; ENOTSUP for another c_dtype.
+ */
+mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
+                                const uint8_t* b_data, const uint8_t* b_scale, void* c,
+                                int32_t c_dtype, int64_t T, int64_t N, int64_t K,
+                                const int64_t* m_splits, int32_t G, void* stream);
+
+/*
+ * mxfp8_validate_splits -- device-side check of the alignment contract on the
+ * device splits ([P3224] review: an alignment check must accompany device
+ * m_splits).  Writes *flag (device int32) = bitmask: 1 = a negative split,
+ * 2 = a split not a multiple of 128, 4 = sum != T.  0 means valid.  The host
+ * reads the flag only when it wants to (no synchronization here).
+ */
+mxfp8_status mxfp8_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,
+                                   void* stream);
+
+/*
+ * SwiGLU between the two linears of the fused expert MLP ([P3545]
+ * Description: FC1 -> activation -> FC2; the activation is not defined on
+ * the pages).  Gate = columns [0, F), up = columns [F, 2F) of h:
+ *   a = silu(gate) * up;  fp32 math, bf16 in and out (round to nearest even).
+ *   h [T, 2F] bf16, a [T, F] bf16.  Errors: EINVAL for NULL, T < 0, F % 8.
+ */
+mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,
+                              void* stream);
+
+/*
+ * Backward of mxfp8_swiglu_fwd: given h [T, 2F] and da [T, F] (bf16), writes
+ * dh [T, 2F] bf16: d gate = da * up * s * (1 + gate * (1 - s)), s = sigmoid(gate);
+ * d up = da * silu(gate).  Errors as mxfp8_swiglu_fwd.
+ */
+mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
+                              uint16_t* dh, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8MOE_H */

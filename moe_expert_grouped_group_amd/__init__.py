@@ -1,0 +1,13 @@
+"""MXFP8 MoE expert grouped-GEMM hot path for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``libmxfp8moe.so`` (include/mxfp8moe.h); this package is the thin Python
+binding over it (torch supplies device memory and streams) plus the seeded
+input generators.
+"""
+
+from .binding import (  # noqa: F401
+    COLWISE, LAYOUT_NN, LAYOUT_NT, LAYOUT_TN, ROWWISE, MXFP8Tensor, dbias_workspace_bytes,
+    group_quantize, grouped_dbias, grouped_gemm, requant_colwise, swiglu_bwd, swiglu_fwd,
+    validate_splits)
+from ._native import load as load_library, lib_path  # noqa: F401

@@ -1,0 +1,201 @@
+// C-ABI entry points of libmxfp8moe.so: argument validation, then kernel
+// launches on the caller's stream.  Nothing here allocates, frees or
+// synchronizes.  The contracts are documented in include/mxfp8moe.h.
+#include "../../include/mxfp8moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mxfp8_status fail(mxfp8_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mxfp8_status ok() {
+  g_err[0] = '\0';
+  return MXFP8_OK;
+}
+
+mxfp8_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MXFP8_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define REQUIRE(cond, ...)                                 \
+  do {                                                     \
+    if (!(cond)) return fail(MXFP8_EINVAL, __VA_ARGS__);   \
+  } while (0)
+
+// The native grouped path takes device-resident int64 splits; a host array is
+// an error (mirrors the ValueError for host m_splits in "Improve device-init
+// grouped linear module with single grouped weight support").
+mxfp8_status check_device_splits(const int64_t* m_splits, int32_t G, const char* fn) {
+  if (m_splits == nullptr) return fail(MXFP8_EINVAL, "%s: m_splits is NULL", fn);
+  if (G < 1) return fail(MXFP8_EINVAL, "%s: G = %d must be >= 1", fn, (int)G);
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  const hipError_t e = hipPointerGetAttributes(&attr, m_splits);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return fail(MXFP8_EINVAL,
+                "%s: m_splits must be a device int64 array (pointer query failed: %s)", fn,
+                hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(MXFP8_EINVAL, "%s: m_splits must be a device int64 array, got a host pointer",
+                fn);
+  return MXFP8_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp8_last_error(void) { return g_err; }
+
+int32_t mxfp8_abi_version(void) { return 1; }
+
+size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N) {
+  if (T <= 0 || N <= 0) return 0;
+  return (size_t)((T + 127) / 128) * (size_t)N * sizeof(float);
+}
+
+mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint32_t usage,
+                                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                  uint8_t* s_col, void* stream) {
+  const char* fn = "mxfp8_group_quantize";
+  REQUIRE(x != nullptr, "%s: x is NULL", fn);
+  REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
+          "%s: usage must be a non-empty combination of MXFP8_ROWWISE and MXFP8_COLWISE", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
+  REQUIRE(!row || (q_row && s_row), "%s: ROWWISE requested but q_row/s_row is NULL", fn);
+  REQUIRE(!col || (q_col && s_col), "%s: COLWISE requested but q_col/s_col is NULL", fn);
+  if (T == 0) return ok();
+  hipError_t e;
+  if (col)
+    e = mx::launch_quant_rowcol(x, T, K, row ? q_row : nullptr, row ? s_row : nullptr, q_col,
+                                s_col, as_stream(stream));
+  else
+    e = mx::launch_quant_rowwise(x, T, K, q_row, s_row, as_stream(stream));
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                   int64_t K, uint8_t* q_col, uint8_t* s_col,
+                                   const int64_t* m_splits, int32_t G, float* dbias,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mxfp8_requant_colwise";
+  REQUIRE(q_row && s_row && q_col && s_col, "%s: NULL data/scale pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  float* partial = nullptr;
+  if (dbias != nullptr) {
+    mxfp8_status st = check_device_splits(m_splits, G, fn);
+    if (st != MXFP8_OK) return st;
+    REQUIRE(workspace != nullptr && workspace_bytes >= mxfp8_dbias_workspace_bytes(T, K),
+            "%s: dbias needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, K));
+    partial = static_cast<float*>(workspace);
+  }
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0) e = mx::launch_requant_colwise(q_row, s_row, T, K, q_col, s_col, partial, st);
+  if (e == hipSuccess && dbias != nullptr)
+    e = mx::launch_dbias_finalize(partial, m_splits, G, K, dbias, st);
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                 int64_t N, const int64_t* m_splits, int32_t G, float* dbias,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mxfp8_grouped_dbias";
+  REQUIRE(q_row && s_row && dbias, "%s: NULL pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
+          (long long)N);
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  REQUIRE(workspace != nullptr && workspace_bytes >= mxfp8_dbias_workspace_bytes(T, N),
+          "%s: needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, N));
+  float* partial = static_cast<float*>(workspace);
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0) e = mx::launch_dbias_partial(q_row, s_row, T, N, partial, st);
+  if (e == hipSuccess) e = mx::launch_dbias_finalize(partial, m_splits, G, N, dbias, st);
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
+                                const uint8_t* b_data, const uint8_t* b_scale, void* c,
+                                int32_t c_dtype, int64_t T, int64_t N, int64_t K,
+                                const int64_t* m_splits, int32_t G, void* stream) {
+  const char* fn = "mxfp8_grouped_gemm";
+  REQUIRE(layout == MXFP8_LAYOUT_NT || layout == MXFP8_LAYOUT_NN || layout == MXFP8_LAYOUT_TN,
+          "%s: layout %d is not NT(0), NN(1) or TN(2)", fn, (int)layout);
+  if (c_dtype != MXFP8_OUT_F32 && c_dtype != MXFP8_OUT_BF16)
+    return fail(MXFP8_ENOTSUP, "%s: output dtype %d is not supported (f32 = 0, bf16 = 1)", fn,
+                (int)c_dtype);
+  REQUIRE(a_data && a_scale && b_data && b_scale && c, "%s: NULL operand pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
+          (long long)N);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  REQUIRE(G <= 1024, "%s: G = %d exceeds the supported 1024 experts", fn, (int)G);
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  if (T == 0 && layout != MXFP8_LAYOUT_TN) return ok();
+  const hipError_t e = mx::launch_grouped_gemm(layout, a_data, a_scale, b_data, b_scale, c,
+                                               c_dtype == MXFP8_OUT_BF16, T, N, K, m_splits, G,
+                                               as_stream(stream));
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,
+                                   void* stream) {
+  const char* fn = "mxfp8_validate_splits";
+  REQUIRE(flag != nullptr, "%s: flag is NULL", fn);
+  REQUIRE(G <= 1 << 20, "%s: G = %d is too large", fn, (int)G);
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  return hip_status(mx::launch_validate_splits(m_splits, G, T, flag, as_stream(stream)), fn);
+}
+
+mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,
+                              void* stream) {
+  const char* fn = "mxfp8_swiglu_fwd";
+  REQUIRE(h && a, "%s: NULL pointer", fn);
+  REQUIRE(T >= 0, "%s: T < 0", fn);
+  REQUIRE(F > 0 && F % 8 == 0, "%s: F = %lld must be a positive multiple of 8", fn, (long long)F);
+  if (T == 0) return ok();
+  return hip_status(mx::launch_swiglu_fwd(h, T, F, a, as_stream(stream)), fn);
+}
+
+mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
+                              uint16_t* dh, void* stream) {
+  const char* fn = "mxfp8_swiglu_bwd";
+  REQUIRE(h && da && dh, "%s: NULL pointer", fn);
+  REQUIRE(T >= 0, "%s: T < 0", fn);
+  REQUIRE(F > 0 && F % 8 == 0, "%s: F = %lld must be a positive multiple of 8", fn, (long long)F);
+  if (T == 0) return ok();
+  return hip_status(mx::launch_swiglu_bwd(h, da, T, F, dh, as_stream(stream)), fn);
+}
+
+}  // extern "C"

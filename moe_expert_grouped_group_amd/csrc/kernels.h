@@ -1,0 +1,32 @@
+// Internal launcher declarations (host side).  Each launcher enqueues its
+// kernels on `st` and returns hipGetLastError(); shapes are validated by the
+// C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t T, int64_t K, uint8_t* q, uint8_t* s,
+                                hipStream_t st);
+hipError_t launch_quant_rowcol(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
+                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st);
+hipError_t launch_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                  int64_t K, uint8_t* q_col, uint8_t* s_col, float* partial,
+                                  hipStream_t st);
+hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int64_t T, int64_t N,
+                                float* partial, hipStream_t st);
+hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,
+                                 int64_t K, float* dbias, hipStream_t st);
+hipError_t launch_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,
+                                  hipStream_t st);
+hipError_t launch_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,
+                             hipStream_t st);
+hipError_t launch_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
+                             uint16_t* dh, hipStream_t st);
+hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                               const uint8_t* sb, void* c, bool out_bf16, int64_t T, int64_t N,
+                               int64_t K, const int64_t* m_splits, int32_t G, hipStream_t st);
+
+}  // namespace mx

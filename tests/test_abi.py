@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports what the header declares, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.lib_path()):
+        from moe_expert_grouped_group_amd import build
+        build.build()
+    return _native.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp8_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding declares a signature for each of them
+    assert sorted(_native.SIGNATURES) == names
+
+
+def test_only_one_hip_runtime(lib):
+    assert len(_native._hip_runtimes_mapped()) <= 1
+
+
+def test_abi_version_and_workspace(lib):
+    assert lib.mxfp8_abi_version() == _native.ABI_VERSION
+    assert lib.mxfp8_dbias_workspace_bytes(16384, 14336) == 128 * 14336 * 4
+    assert lib.mxfp8_dbias_workspace_bytes(0, 512) == 0
+
+
+def _status_msg(lib, st):
+    return st, lib.mxfp8_last_error().decode()
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_quantize_rejects(lib):
+    q = lib.mxfp8_group_quantize
+    assert _status_msg(lib, q(None, 128, 512, 1, FAKE, FAKE, None, None, None))[0] == 1
+    st, msg = _status_msg(lib, q(FAKE, 100, 512, 1, FAKE, FAKE, None, None, None))
+    assert st == 1 and "128" in msg
+    st, msg = _status_msg(lib, q(FAKE, 128, 96, 1, FAKE, FAKE, None, None, None))
+    assert st == 1 and "512" in msg
+    assert q(FAKE, 128, 512, 0, FAKE, FAKE, None, None, None) == 1          # no usage
+    assert q(FAKE, 128, 512, 4, FAKE, FAKE, None, None, None) == 1          # unknown usage bit
+    assert q(FAKE, 128, 512, 2, FAKE, FAKE, None, None, None) == 1          # col without buffers
+    assert q(FAKE, 128, 512, 1, None, FAKE, None, None, None) == 1          # row without data
+
+
+def test_gemm_rejects(lib):
+    g = lib.mxfp8_grouped_gemm
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert g(3, *args, 0, 128, 512, 512, FAKE, 1, None) == 1                 # bad layout
+    st, msg = _status_msg(lib, g(0, *args, 7, 128, 512, 512, FAKE, 1, None))
+    assert st == 2 and "dtype" in msg                                        # NotImplemented
+    assert g(0, None, FAKE, FAKE, FAKE, FAKE, 0, 128, 512, 512, FAKE, 1, None) == 1
+    assert g(0, *args, 0, 129, 512, 512, FAKE, 1, None) == 1                # T % 128
+    assert g(0, *args, 0, 128, 500, 512, FAKE, 1, None) == 1                # N % 512
+    assert g(0, *args, 0, 128, 512, 256, FAKE, 1, None) == 1                # K % 512
+    assert g(0, *args, 0, 128, 512, 512, None, 1, None) == 1                # no splits
+    assert g(0, *args, 0, 128, 512, 512, FAKE, 0, None) == 1                # G < 1
+
+
+def test_gemm_rejects_host_splits(lib):
+    splits = np.array([128], dtype=np.int64)
+    st, msg = _status_msg(lib, lib.mxfp8_grouped_gemm(
+        0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 512, 512,
+        splits.ctypes.data_as(ctypes.c_void_p), 1, None))
+    assert st == 1 and "m_splits" in msg
+
+
+def test_requant_and_dbias_reject(lib):
+    r = lib.mxfp8_requant_colwise
+    assert r(None, FAKE, 128, 512, FAKE, FAKE, None, 0, None, None, 0, None) == 1
+    assert r(FAKE, FAKE, 128, 100, FAKE, FAKE, None, 0, None, None, 0, None) == 1
+    # dbias requested without splits / workspace
+    assert r(FAKE, FAKE, 128, 512, FAKE, FAKE, None, 1, FAKE, FAKE, 1 << 20, None) == 1
+    d = lib.mxfp8_grouped_dbias
+    assert d(FAKE, FAKE, 128, 512, None, 1, FAKE, FAKE, 1 << 20, None) == 1
+    assert d(FAKE, FAKE, 130, 512, FAKE, 1, FAKE, FAKE, 1 << 20, None) == 1
+
+
+def test_swiglu_and_validate_reject(lib):
+    assert lib.mxfp8_swiglu_fwd(None, 4, 8, FAKE, None) == 1
+    assert lib.mxfp8_swiglu_fwd(FAKE, 4, 6, FAKE, None) == 1
+    assert lib.mxfp8_swiglu_bwd(FAKE, None, 4, 8, FAKE, None) == 1
+    assert lib.mxfp8_validate_splits(FAKE, 1, 128, None, None) == 1
+
+
+def test_binding_maps_errors(lib):
+    with pytest.raises(ValueError):
+        _native.check(1, "x")
+    with pytest.raises(NotImplementedError):
+        _native.check(2, "x")
+    with pytest.raises(RuntimeError):
+        _native.check(3, "x")
+    assert mx.ROWWISE == 1 and mx.COLWISE == 2

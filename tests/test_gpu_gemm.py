@@ -1,0 +1,176 @@
+"""GPU parity of the grouped MXFP8 GEMMs (forward NT, dgrad NN, wgrad TN)
+against the CPU oracle.
+
+fp32 outputs: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k| + 1e-6 per element;
+bf16 outputs: within 1 bf16 ulp of the oracle rounded to bf16, widened by the
+same fp32 accumulation allowance for outputs that cancel; integer-valued
+operands with unit scales: exactly equal.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import workloads as wl
+from oracle import gemm as og
+from oracle import mxfp8 as om
+
+from gpu_util import dev, f64, log, random_mx, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(got, ref, mag, out_dtype):
+    if out_dtype == torch.float32:
+        err = np.abs(got - ref)
+        tol = og.tolerance_f32(mag)
+        bad = err > tol
+        assert not bad.any(), (int(bad.sum()), float((err / tol).max()))
+    else:
+        ok = og.within_bf16_ulp(got, ref, mag)
+        assert ok.all(), int((~ok).sum())
+
+
+def _mx_rows(rng, rows, cols, kind):
+    if kind == "random":
+        return random_mx(rng, rows, cols)
+    # integer-valued codes (|v| <= 16) with unit scales: fp32 sums are exact
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50, 0x51, 0x52, 0x53,
+                     0x54, 0x55, 0x56, 0x57, 0x58], dtype=np.uint8)   # 0, 1, 2, ..., 16
+    q = ints[rng.integers(0, ints.size, size=(rows, cols))]
+    q |= (rng.integers(0, 2, size=(rows, cols)) << 7).astype(np.uint8)
+    s = np.full((rows, cols // 32), 127, dtype=np.uint8)
+    return q, s
+
+
+CASES = [
+    # (splits, N, K)
+    ([128, 256, 0, 384], 512, 512),
+    ([512], 1024, 512),
+    ([0, 128, 0, 0, 640, 128, 256, 0], 512, 1024),
+]
+
+
+@pytest.mark.parametrize("kind", ["random", "integer"])
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_three_layouts_synthetic(kind, case, out_dtype):
+    splits, n, k = CASES[case]
+    g = len(splits)
+    t = sum(splits)
+    rng = np.random.default_rng(1000 + case)
+    xq, xs = _mx_rows(rng, t, k, kind)
+    wq, ws = _mx_rows(rng, g * n, k, kind)
+    dyq, dys = _mx_rows(rng, t, n, kind)
+    wcq, wcs = _mx_rows(rng, k, g * n, kind)         # any valid column-wise copy
+    dycq, dycs = _mx_rows(rng, n, t, kind)
+    xcq, xcs = _mx_rows(rng, k, t, kind)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+
+    log(f"gemm NT {kind} case {case} {out_dtype}")
+    y = mx.grouped_gemm("NT", dev(xq), dev(xs), dev(wq), dev(ws), ms, t, n, k, out_dtype)
+    log(f"gemm NN {kind} case {case} {out_dtype}")
+    dx = mx.grouped_gemm("NN", dev(dyq), dev(dys), dev(wcq), dev(wcs), ms, t, n, k, out_dtype)
+    log(f"gemm TN {kind} case {case} {out_dtype}")
+    dw = mx.grouped_gemm("TN", dev(dycq), dev(dycs), dev(xcq), dev(xcs), ms, t, n, k, out_dtype)
+    torch.cuda.synchronize()
+
+    ref, mag = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits, True)
+    ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, splits, g, True)
+    ref3, mag3 = og.wgrad(dycq, dycs, xcq, xcs, splits, True)
+    if kind == "integer" and out_dtype == torch.float32:
+        assert np.array_equal(f64(y), ref)
+        assert np.array_equal(f64(dx), ref2)
+        assert np.array_equal(f64(dw), ref3)
+    else:
+        _check(f64(y), ref, mag, out_dtype)
+        _check(f64(dx), ref2, mag2, out_dtype)
+        _check(f64(dw), ref3, mag3, out_dtype)
+    for gi, m in enumerate(splits):
+        if m == 0:
+            assert np.all(f64(dw)[gi] == 0)
+
+
+def test_single_group_is_dense():
+    rng = np.random.default_rng(5)
+    t, n, k = 384, 512, 1024
+    xq, xs = random_mx(rng, t, k)
+    wq, ws = random_mx(rng, n, k)
+    log("gemm single group")
+    y = mx.grouped_gemm("NT", dev(xq), dev(xs), dev(wq), dev(ws),
+                        dev(np.array([t], dtype=np.int64)), t, n, k)
+    torch.cuda.synchronize()
+    xh, wh = om.dequantize_rowwise(xq, xs), om.dequantize_rowwise(wq, ws)
+    _check(f64(y), xh @ wh.T, np.abs(xh) @ np.abs(wh).T, torch.float32)
+
+
+def test_rows_outside_experts_untouched():
+    # forward writes only the rows of its experts; a canary value elsewhere in
+    # a larger buffer (rows past T) survives
+    rng = np.random.default_rng(6)
+    splits, n, k = [128, 0, 256], 512, 512
+    t = sum(splits)
+    xq, xs = random_mx(rng, t, k)
+    wq, ws = random_mx(rng, 3 * n, k)
+    big = torch.full((t + 128, n), 12345.0, device="cuda")
+    log("gemm canary")
+    mx.grouped_gemm("NT", dev(xq), dev(xs), dev(wq), dev(ws),
+                    dev(np.asarray(splits, dtype=np.int64)), t, n, k, out=big[:t])
+    torch.cuda.synchronize()
+    assert torch.all(big[t:] == 12345.0)
+    ref, mag = og.fprop(xq, xs, wq.reshape(3, n, k), ws.reshape(3, n, k // 32), splits, True)
+    _check(f64(big[:t]), ref, mag, torch.float32)
+
+
+@pytest.mark.parametrize("name", ["tiny_fwd", "small_moe8", "small_skewed", "small_nemotron_mlp"])
+def test_workload_fwd_bwd(name):
+    """The hot path on a workload recipe: quantize, forward, requant, dgrad, wgrad."""
+    w = wl.make(name)
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    ms = dev(w.m_splits)
+    splits = [int(v) for v in w.m_splits]
+    log(f"workload {name}: quantize")
+    xo = mx.group_quantize(w.tensors["x"].to("cuda"), mx.ROWWISE)
+    wo = mx.group_quantize(w.tensors["w"].to("cuda"), mx.ROWWISE | mx.COLWISE)
+    log(f"workload {name}: forward")
+    y = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
+                        out_dtype)
+    torch.cuda.synchronize()
+    xq, xs = u8(xo.row_data), u8(xo.row_scale)
+    wq, ws = u8(wo.row_data), u8(wo.row_scale)
+    ref, mag = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits, True)
+    _check(f64(y), ref, mag, out_dtype)
+    if name == "tiny_fwd":
+        return
+    dy_t = w.tensors["dy"]
+    if dy_t.shape[1] != n:     # fused-MLP workloads carry the FC2 gradient; use an FC1-shaped one
+        dy_t = wl.bf16_normal([w.wid, wl.STREAM_DY, 99], (t, n))
+    log(f"workload {name}: backward")
+    dyo = mx.group_quantize(dy_t.to("cuda"), mx.ROWWISE)
+    xo2, _db_x = mx.requant_colwise(xo.row_data, xo.row_scale, ms, with_dbias=True)
+    dyo2, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True)
+    dx = mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n,
+                         k, out_dtype)
+    dw = mx.grouped_gemm("TN", dyo2.col_data, dyo2.col_scale, xo2.col_data, xo2.col_scale, ms,
+                         t, n, k, out_dtype)
+    torch.cuda.synchronize()
+    dyq, dys = u8(dyo.row_data), u8(dyo.row_scale)
+    # column-wise copies: bit-exact against the oracle's requant
+    qc, sc = om.requant_colwise(dyq, dys, splits)
+    assert np.array_equal(u8(dyo2.col_data), qc) and np.array_equal(u8(dyo2.col_scale), sc)
+    qc, sc = om.requant_colwise(xq, xs, splits)
+    assert np.array_equal(u8(xo2.col_data), qc) and np.array_equal(u8(xo2.col_scale), sc)
+    ref2, mag2 = og.dgrad(dyq, dys, u8(wo.col_data), u8(wo.col_scale), splits, g, True)
+    _check(f64(dx), ref2, mag2, out_dtype)
+    ref3, mag3 = og.wgrad(u8(dyo2.col_data), u8(dyo2.col_scale), u8(xo2.col_data),
+                          u8(xo2.col_scale), splits, True)
+    _check(f64(dw), ref3, mag3, out_dtype)
+    refb = om.grouped_dbias(dyq, dys, splits)
+    xh = np.abs(om.dequantize_rowwise(dyq, dys))
+    row = 0
+    for gi, m in enumerate(splits):
+        magb = xh[row:row + m].sum(axis=0)
+        assert np.all(np.abs(f64(db)[gi] - refb[gi]) <= og.tolerance_f32(magb))
+        row += m

@@ -1,0 +1,201 @@
+"""GPU parity of the streaming kernels against the CPU oracle.
+
+Quantized bytes and scales must be bit-exact; dbias (fp32 sums) must be
+within 1e-5 * sum|x| + 1e-6; SwiGLU (bf16 out) within 1 bf16 ulp of the
+oracle rounded to bf16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import workloads as wl
+from oracle import gemm as og
+from oracle import mxfp8 as om
+from oracle import swiglu as osw
+
+from gpu_util import (all_bf16_bits, bf16_from_bits, dev, f64, log, random_mx, sweep_bf16_bits,
+                      u8)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_row(x_cpu_bf16, out):
+    q, s = om.quantize_rowwise(f64(x_cpu_bf16))
+    assert np.array_equal(u8(out.row_scale), s)
+    assert np.array_equal(u8(out.row_data), q)
+
+
+def _check_col(x_cpu_bf16, out, splits=None):
+    x = f64(x_cpu_bf16)
+    splits = [x.shape[0]] if splits is None else splits
+    q, s = om.quantize_colwise(x, splits)
+    assert np.array_equal(u8(out.col_scale), s)
+    assert np.array_equal(u8(out.col_data), q)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(256, 512, 1), (1024, 1536, 2), (128, 4096, 3)])
+def test_rowwise_sweep(rows, cols, seed):
+    log(f"rowwise sweep {rows}x{cols} seed {seed}")
+    x = bf16_from_bits(sweep_bf16_bits(rows, cols, seed))
+    out = mx.group_quantize(x.to("cuda"), mx.ROWWISE)
+    torch.cuda.synchronize()
+    _check_row(x, out)
+
+
+def test_rowwise_every_bf16_value():
+    log("rowwise every bf16 value")
+    x = bf16_from_bits(all_bf16_bits(512))
+    out = mx.group_quantize(x.to("cuda"), mx.ROWWISE)
+    torch.cuda.synchronize()
+    _check_row(x, out)
+
+
+@pytest.mark.parametrize("usage", [mx.COLWISE, mx.ROWWISE | mx.COLWISE])
+@pytest.mark.parametrize("rows,cols,seed", [(256, 512, 4), (640, 1024, 5)])
+def test_rowcol_sweep(usage, rows, cols, seed):
+    log(f"rowcol sweep usage {usage} {rows}x{cols}")
+    x = bf16_from_bits(sweep_bf16_bits(rows, cols, seed))
+    out = mx.group_quantize(x.to("cuda"), usage)
+    torch.cuda.synchronize()
+    _check_col(x, out)
+    if usage & mx.ROWWISE:
+        _check_row(x, out)
+
+
+def test_rowcol_every_bf16_value():
+    log("rowcol every bf16 value")
+    x = bf16_from_bits(all_bf16_bits(512))
+    out = mx.group_quantize(x.to("cuda"), mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    _check_row(x, out)
+    _check_col(x, out)
+
+
+@pytest.mark.parametrize("name", ["tiny_fwd", "small_moe8", "small_skewed",
+                                  "small_group_quantize", "small_nemotron_mlp"])
+def test_workload_quantize(name):
+    log(f"workload quantize {name}")
+    w = wl.make(name)
+    x = w.tensors["x"]
+    out = mx.group_quantize(x.to("cuda"), mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    _check_row(x, out)
+    _check_col(x, out, list(w.m_splits))
+    if "w" in w.tensors:
+        wt = w.tensors["w"]
+        g, n, k = wt.shape
+        wo = mx.group_quantize(wt.to("cuda"), mx.ROWWISE | mx.COLWISE)
+        torch.cuda.synchronize()
+        _check_row(wt.reshape(g * n, k), wo)
+        _check_col(wt.reshape(g * n, k), wo)
+
+
+def test_preallocated_outputs_reused():
+    log("preallocated outputs reused")
+    x1 = bf16_from_bits(sweep_bf16_bits(256, 512, 7))
+    x2 = bf16_from_bits(sweep_bf16_bits(256, 512, 8))
+    out = mx.group_quantize(x1.to("cuda"), mx.ROWWISE | mx.COLWISE)
+    ptrs = (out.row_data.data_ptr(), out.col_data.data_ptr())
+    out = mx.group_quantize(x2.to("cuda"), mx.ROWWISE | mx.COLWISE, out=out)
+    torch.cuda.synchronize()
+    assert (out.row_data.data_ptr(), out.col_data.data_ptr()) == ptrs
+    _check_row(x2, out)
+    _check_col(x2, out)
+
+
+def _requant_case(q, s, splits, seed):
+    log(f"requant {q.shape} splits {splits[:6]} seed {seed}")
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    out, db = mx.requant_colwise(dev(q), dev(s), ms, with_dbias=True)
+    torch.cuda.synchronize()
+    qc, sc = om.requant_colwise(q, s, splits)
+    assert np.array_equal(u8(out.col_scale), sc)
+    assert np.array_equal(u8(out.col_data), qc)
+    ref = om.grouped_dbias(q, s, splits)
+    mag = np.zeros_like(ref)
+    xh = np.abs(om.dequantize_rowwise(q, s))
+    row = 0
+    for g, m in enumerate(splits):
+        mag[g] = xh[row:row + m].sum(axis=0)
+        row += m
+    got = f64(db)
+    assert np.all(np.abs(got - ref) <= og.tolerance_f32(mag))
+    for g, m in enumerate(splits):
+        if m == 0:
+            assert np.all(got[g] == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_requant_random_codes(seed):
+    rng = np.random.default_rng(100 + seed)
+    splits = [256, 0, 128, 384, 0, 256]
+    q, s = random_mx(rng, sum(splits), 1024)
+    _requant_case(q, s, splits, seed)
+
+
+def test_requant_wide_scales():
+    # scale bytes spread over the whole E8M0 range used by bf16 data
+    rng = np.random.default_rng(7)
+    splits = [512, 128]
+    q, s = random_mx(rng, 640, 512, smin=0, smax=240)
+    q[:, :64] = 0        # zero column blocks
+    _requant_case(q, s, splits, 7)
+
+
+def test_requant_of_quantized_sweep():
+    x = bf16_from_bits(sweep_bf16_bits(512, 512, 9))
+    q, s = om.quantize_rowwise(f64(x))
+    # keep the values small enough for fp32 dbias sums (exponent fields < 200)
+    s = np.minimum(s, 200).astype(np.uint8)
+    _requant_case(q, s, [128, 256, 128], 9)
+
+
+def test_requant_without_dbias_matches():
+    rng = np.random.default_rng(11)
+    q, s = random_mx(rng, 384, 512)
+    log("requant without dbias")
+    out = mx.requant_colwise(dev(q), dev(s))
+    torch.cuda.synchronize()
+    qc, sc = om.requant_colwise(q, s, [384])
+    assert np.array_equal(u8(out.col_data), qc) and np.array_equal(u8(out.col_scale), sc)
+
+
+@pytest.mark.parametrize("splits", [[128, 0, 256, 128], [512], [0, 0, 384]])
+def test_grouped_dbias(splits):
+    log(f"grouped dbias {splits}")
+    rng = np.random.default_rng(sum(splits))
+    q, s = random_mx(rng, sum(splits), 1024)
+    db = mx.grouped_dbias(dev(q), dev(s), dev(np.asarray(splits, dtype=np.int64)))
+    torch.cuda.synchronize()
+    ref = om.grouped_dbias(q, s, splits)
+    xh = np.abs(om.dequantize_rowwise(q, s))
+    row = 0
+    got = f64(db)
+    for g, m in enumerate(splits):
+        mag = xh[row:row + m].sum(axis=0)
+        assert np.all(np.abs(got[g] - ref[g]) <= og.tolerance_f32(mag))
+        row += m
+
+
+def test_validate_splits():
+    log("validate splits")
+    cases = [([128, 256, 0], 384, 0), ([128, 100], 228, 2), ([-128, 256], 128, 1),
+             ([128, 128], 512, 4), ([130, -2], 128, 3)]
+    for splits, t, want in cases:
+        flag = mx.validate_splits(dev(np.asarray(splits, dtype=np.int64)), t)
+        assert int(flag.item()) == want, (splits, t)
+
+
+@pytest.mark.parametrize("t,f", [(256, 1024), (384, 512)])
+def test_swiglu(t, f):
+    log(f"swiglu {t}x{f}")
+    rng = np.random.default_rng(t + f)
+    h = torch.from_numpy((rng.standard_normal((t, 2 * f)) * 3).astype(np.float32)).to(torch.bfloat16)
+    da = torch.from_numpy(rng.standard_normal((t, f)).astype(np.float32)).to(torch.bfloat16)
+    a = mx.swiglu_fwd(h.to("cuda"))
+    dh = mx.swiglu_bwd(h.to("cuda"), da.to("cuda"))
+    torch.cuda.synchronize()
+    assert og.within_bf16_ulp(f64(a), osw.swiglu_fwd(f64(h))).all()
+    assert og.within_bf16_ulp(f64(dh), osw.swiglu_bwd(f64(h), f64(da))).all()

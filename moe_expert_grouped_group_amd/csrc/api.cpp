@@ -118,7 +118,7 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
   hipError_t e = hipSuccess;
   if (T > 0) e = mx::launch_requant_colwise(q_row, s_row, T, K, q_col, s_col, partial, st);
   if (e == hipSuccess && dbias != nullptr)
-    e = mx::launch_dbias_finalize(partial, m_splits, G, K, dbias, st);
+    e = mx::launch_dbias_finalize(partial, m_splits, G, T, K, dbias, st);
   return hip_status(e, fn);
 }
 
@@ -138,7 +138,7 @@ mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int
   hipStream_t st = as_stream(stream);
   hipError_t e = hipSuccess;
   if (T > 0) e = mx::launch_dbias_partial(q_row, s_row, T, N, partial, st);
-  if (e == hipSuccess) e = mx::launch_dbias_finalize(partial, m_splits, G, N, dbias, st);
+  if (e == hipSuccess) e = mx::launch_dbias_finalize(partial, m_splits, G, T, N, dbias, st);
   return hip_status(e, fn);
 }
 

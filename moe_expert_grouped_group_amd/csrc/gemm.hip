@@ -24,8 +24,9 @@
 // tokens owns no forward/dgrad tile and a zero wgrad output.
 //
 // The MFMA used is V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both operands in
-// E4M3: per lane 32 consecutive contraction bytes of one row, one E8M0 scale
-// per lane (the row's 32-element block), fp32 accumulators.
+// E4M3: per lane 32 contraction bytes of one row (two 16-byte runs, see the
+// fragment loads), one E8M0 scale per lane (one 32-element block of the
+// row), fp32 accumulators.
 #include "mx_device.h"
 #include "kernels.h"
 
@@ -79,7 +80,7 @@ __device__ GroupHit find_group(const int64_t* __restrict__ m_splits, int G, int6
 #pragma unroll
   for (int i = 0; i < per; ++i) {
     const int g = tid * per + i;
-    mv[i] = g < G ? m_splits[g] : 0;
+    mv[i] = g < G ? max(m_splits[g], (int64_t)0) : 0;   // negative splits count as empty
     r_sum += mv[i];
     u_sum += TILES ? (mv[i] + BM - 1) / BM : 1;
   }
@@ -152,7 +153,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     if (h.g < 0) return;                        // beyond the last expert's tiles
     m0 = h.off + (int64_t)h.local * BM;
     n0 = (int64_t)nt * BN;
-    valid_rows = min((int64_t)BM, h.off + h.len - m0);
+    // rows of the expert, never past the token count (splits that break the
+    // contract must not make the kernel read or write out of bounds)
+    valid_rows = min(min((int64_t)BM, h.off + h.len - m0), p.rows - m0);
+    if (valid_rows <= 0) return;
     a_base = p.a + m0 * p.lda;
     sa_base = p.sa + m0 * p.ldsa;
     b_base = p.b + h.g * p.b_gstride + n0 * p.ldb;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     sa_base = p.sa + m0 * p.ldsa + h.off / 32;
     b_base = p.b + n0 * p.ldb + h.off;
     sb_base = p.sb + n0 * p.ldsb + h.off / 32;
-    klen = h.len;
+    klen = h.off < p.kc ? min(h.len, p.kc - h.off) : 0;   // p.kc = T here
     c_base = reinterpret_cast<char*>(p.c) + (h.g * p.c_gstride + m0 * p.ldc + n0) * esz;
   }
 
@@ -211,8 +215,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   const int nk = (int)(klen / BK);
   u32x4 ra[4], rb[4];
   uint32_t rs = 0;
-  // fragment addresses: operand row (l % 16) of a 16-row sub-tile, bytes
-  // [32 (l/16), 32 (l/16) + 32) = chunks 2(l/16) and 2(l/16)+1
+  // fragment addresses: operand row (l % 16) of a 16-row sub-tile.  The
+  // instruction takes, in lane l with q = l/16, the contraction bytes
+  // [16q, 16q+16) in its first 16 bytes and [64+16q, 64+16q+16) in its last
+  // 16 (16-byte chunks q and 4+q of the 128-byte stage); the lane's scale
+  // byte is that of 32-element block q of its row.
   const int fr = lane & 15;
   const int fq = lane >> 4;
 
@@ -250,16 +257,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 64 + i * 16 + fr;
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + swz(r, 2 * fq));
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + swz(r, 2 * fq + 1));
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + swz(r, fq));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + swz(r, 4 + fq));
       af[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       as[i] = base[2 * kTileBytes + r * 4 + fq];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 64 + j * 16 + fr;
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, 2 * fq));
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, 2 * fq + 1));
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, fq));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, 4 + fq));
       bf[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       bs[j] = base[2 * kTileBytes + BM * 4 + r * 4 + fq];
     }
@@ -334,7 +341,7 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
     p.lda = T; p.ldsa = T / 32;
     p.ldb = T; p.ldsb = T / 32;
     p.ldc = K; p.c_gstride = N * K;
-    p.rows = N; p.cols = K;
+    p.rows = N; p.cols = K; p.kc = T;
   }
   p.ntiles_n = (int32_t)(p.cols / BN);
   if (!kgrouped) {

@@ -18,7 +18,7 @@ hipError_t launch_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, in
 hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int64_t T, int64_t N,
                                 float* partial, hipStream_t st);
 hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,
-                                 int64_t K, float* dbias, hipStream_t st);
+                                 int64_t T, int64_t K, float* dbias, hipStream_t st);
 hipError_t launch_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,
                                   hipStream_t st);
 hipError_t launch_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,

@@ -329,13 +329,13 @@ __global__ __launch_bounds__(256) void dbias_partial_kernel(
 // dbias[g, k] = sum over the 128-row tiles of expert g of partial[tile, k],
 // in tile order.  grid = (G, ceil(K / 256)).
 __global__ __launch_bounds__(256) void dbias_finalize_kernel(
-    const float* __restrict__ partial, const int64_t* __restrict__ m_splits, int32_t G, int64_t K,
-    float* __restrict__ dbias) {
+    const float* __restrict__ partial, const int64_t* __restrict__ m_splits, int32_t G, int64_t T,
+    int64_t K, float* __restrict__ dbias) {
   __shared__ int64_t red[256];
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t acc = 0;
-  for (int i = tid; i < g; i += 256) acc += m_splits[i];
+  for (int i = tid; i < g; i += 256) acc += max(m_splits[i], (int64_t)0);
   red[tid] = acc;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -343,11 +343,14 @@ __global__ __launch_bounds__(256) void dbias_finalize_kernel(
     __syncthreads();
   }
   const int64_t off = red[0];
-  const int64_t mg = m_splits[g];
+  const int64_t mg = max(m_splits[g], (int64_t)0);
   const int64_t k = (int64_t)blockIdx.y * 256 + tid;
   if (k >= K) return;
+  // tiles of the expert, clipped to the token count (splits that break the
+  // contract must not make the kernel read out of bounds)
+  const int64_t first = min(off, T) / kTileT, last = min(off + mg, T) / kTileT;
   float s = 0.f;
-  for (int64_t tile = off / kTileT; tile < (off + mg) / kTileT; ++tile) s += partial[tile * K + k];
+  for (int64_t tile = first; tile < last; ++tile) s += partial[tile * K + k];
   dbias[(int64_t)g * K + k] = s;
 }
 
@@ -474,9 +477,9 @@ hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int6
 }
 
 hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,
-                                 int64_t K, float* dbias, hipStream_t st) {
+                                 int64_t T, int64_t K, float* dbias, hipStream_t st) {
   dim3 grid((unsigned)G, (unsigned)((K + 255) / 256));
-  hipLaunchKernelGGL(dbias_finalize_kernel, grid, dim3(256), 0, st, partial, m_splits, G, K,
+  hipLaunchKernelGGL(dbias_finalize_kernel, grid, dim3(256), 0, st, partial, m_splits, G, T, K,
                      dbias);
   return hipGetLastError();
 }

@@ -1,10 +1,16 @@
 """GPU parity of the grouped MXFP8 GEMMs (forward NT, dgrad NN, wgrad TN)
 against the CPU oracle.
 
-fp32 outputs: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k| + 1e-6 per element;
-bf16 outputs: within 1 bf16 ulp of the oracle rounded to bf16, widened by the
-same fp32 accumulation allowance for outputs that cancel; integer-valued
-operands with unit scales: exactly equal.
+fp32 outputs of forward and dgrad on well-scaled data (the Gaussian
+workloads, contractions of 512 and more): |gpu - oracle| <= 1e-5 * sum_k
+|a_k b_k| + 1e-6 per element.  Everywhere else (wgrad, whose contraction is
+one expert's few 128-token windows; outliers; random codes over the whole
+E4M3 range with random block scales) the bound adds the MFMA window term of
+oracle.gemm.tolerance_mfma, derived from the measured accumulation of the
+scaled MFMA (pinned by test_gpu_mfma_accumulation.py).  bf16 outputs: within
+1 bf16 ulp of the oracle rounded to bf16, widened by the same accumulation
+allowance for outputs that cancel.  Integer-valued operands with unit scales:
+exactly equal.
 """
 
 import numpy as np
@@ -21,14 +27,15 @@ from gpu_util import dev, f64, log, random_mx, u8
 pytestmark = pytest.mark.gpu
 
 
-def _check(got, ref, mag, out_dtype):
+def _check(got, ref, mag, out_dtype, win=None):
+    """win None: the 1e-5 rule; else the MFMA window bound (tolerance_mfma)."""
+    tol = og.tolerance_f32(mag) if win is None else og.tolerance_mfma(mag, win)
     if out_dtype == torch.float32:
         err = np.abs(got - ref)
-        tol = og.tolerance_f32(mag)
         bad = err > tol
         assert not bad.any(), (int(bad.sum()), float((err / tol).max()))
     else:
-        ok = og.within_bf16_ulp(got, ref, mag)
+        ok = og.within_bf16_ulp(got, ref, tol)
         assert ok.all(), int((~ok).sum())
 
 
@@ -76,17 +83,19 @@ def test_three_layouts_synthetic(kind, case, out_dtype):
     dw = mx.grouped_gemm("TN", dev(dycq), dev(dycs), dev(xcq), dev(xcs), ms, t, n, k, out_dtype)
     torch.cuda.synchronize()
 
-    ref, mag = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits, True)
-    ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, splits, g, True)
-    ref3, mag3 = og.wgrad(dycq, dycs, xcq, xcs, splits, True)
+    ref, mag, win = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits,
+                             True, True)
+    ref2, mag2, win2 = og.dgrad(dyq, dys, wcq, wcs, splits, g, True, True)
+    ref3, mag3, win3 = og.wgrad(dycq, dycs, xcq, xcs, splits, True, True)
     if kind == "integer" and out_dtype == torch.float32:
         assert np.array_equal(f64(y), ref)
         assert np.array_equal(f64(dx), ref2)
         assert np.array_equal(f64(dw), ref3)
     else:
-        _check(f64(y), ref, mag, out_dtype)
-        _check(f64(dx), ref2, mag2, out_dtype)
-        _check(f64(dw), ref3, mag3, out_dtype)
+        # random codes span the whole E4M3 range with random block scales
+        _check(f64(y), ref, mag, out_dtype, win)
+        _check(f64(dx), ref2, mag2, out_dtype, win2)
+        _check(f64(dw), ref3, mag3, out_dtype, win3)
     for gi, m in enumerate(splits):
         if m == 0:
             assert np.all(f64(dw)[gi] == 0)
@@ -101,8 +110,10 @@ def test_single_group_is_dense():
     y = mx.grouped_gemm("NT", dev(xq), dev(xs), dev(wq), dev(ws),
                         dev(np.array([t], dtype=np.int64)), t, n, k)
     torch.cuda.synchronize()
+    ref, mag, win = og.fprop(xq, xs, wq[None], ws[None], [t], True, True)
     xh, wh = om.dequantize_rowwise(xq, xs), om.dequantize_rowwise(wq, ws)
-    _check(f64(y), xh @ wh.T, np.abs(xh) @ np.abs(wh).T, torch.float32)
+    assert np.array_equal(ref, xh @ wh.T)
+    _check(f64(y), ref, mag, torch.float32, win)
 
 
 def test_rows_outside_experts_untouched():
@@ -119,8 +130,9 @@ def test_rows_outside_experts_untouched():
                     dev(np.asarray(splits, dtype=np.int64)), t, n, k, out=big[:t])
     torch.cuda.synchronize()
     assert torch.all(big[t:] == 12345.0)
-    ref, mag = og.fprop(xq, xs, wq.reshape(3, n, k), ws.reshape(3, n, k // 32), splits, True)
-    _check(f64(big[:t]), ref, mag, torch.float32)
+    ref, mag, win = og.fprop(xq, xs, wq.reshape(3, n, k), ws.reshape(3, n, k // 32), splits,
+                             True, True)
+    _check(f64(big[:t]), ref, mag, torch.float32, win)
 
 
 @pytest.mark.parametrize("name", ["tiny_fwd", "small_moe8", "small_skewed", "small_nemotron_mlp"])
@@ -129,6 +141,7 @@ def test_workload_fwd_bwd(name):
     w = wl.make(name)
     g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
     out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    outliers = "skewed" in name      # X carries 0.1 % outliers x1000
     ms = dev(w.m_splits)
     splits = [int(v) for v in w.m_splits]
     log(f"workload {name}: quantize")
@@ -140,8 +153,9 @@ def test_workload_fwd_bwd(name):
     torch.cuda.synchronize()
     xq, xs = u8(xo.row_data), u8(xo.row_scale)
     wq, ws = u8(wo.row_data), u8(wo.row_scale)
-    ref, mag = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits, True)
-    _check(f64(y), ref, mag, out_dtype)
+    ref, mag, win = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits,
+                             True, True)
+    _check(f64(y), ref, mag, out_dtype, win if outliers else None)
     if name == "tiny_fwd":
         return
     dy_t = w.tensors["dy"]
@@ -164,9 +178,12 @@ def test_workload_fwd_bwd(name):
     assert np.array_equal(u8(xo2.col_data), qc) and np.array_equal(u8(xo2.col_scale), sc)
     ref2, mag2 = og.dgrad(dyq, dys, u8(wo.col_data), u8(wo.col_scale), splits, g, True)
     _check(f64(dx), ref2, mag2, out_dtype)
-    ref3, mag3 = og.wgrad(u8(dyo2.col_data), u8(dyo2.col_scale), u8(xo2.col_data),
-                          u8(xo2.col_scale), splits, True)
-    _check(f64(dw), ref3, mag3, out_dtype)
+    ref3, mag3, win3 = og.wgrad(u8(dyo2.col_data), u8(dyo2.col_scale), u8(xo2.col_data),
+                                u8(xo2.col_scale), splits, True, True)
+    # wgrad contracts over one expert's tokens (a few 128-element windows):
+    # the window truncation does not average out, so it is gated on the
+    # window bound even for Gaussian data
+    _check(f64(dw), ref3, mag3, out_dtype, win3)
     refb = om.grouped_dbias(dyq, dys, splits)
     xh = np.abs(om.dequantize_rowwise(dyq, dys))
     row = 0

@@ -422,3 +422,23 @@ def test_swiglu_bwd_finite_difference():
             hm[i, j] -= eps
             num[i, j] = ((osw.swiglu_fwd(hp) - osw.swiglu_fwd(hm)) * da).sum() / (2 * eps)
     assert np.allclose(dh, num, rtol=1e-6, atol=1e-8)
+
+
+def test_window_run_max_bruteforce():
+    from oracle.gemm import _window_run_max
+    rng = np.random.default_rng(28)
+    a = np.abs(rng.standard_normal((3, 256)))
+    b = np.abs(rng.standard_normal((2, 256)))
+    got = _window_run_max(a, b)
+    for i in range(3):
+        for j in range(2):
+            total = 0.0
+            for w0 in (0, 128):
+                runs = [sum(a[i, k] * b[j, k] for k in range(r0, r0 + 8)) for r0 in range(w0, w0 + 128, 8)]
+                total += max(runs)
+            assert got[i, j] == pytest.approx(total, rel=1e-12)
+
+
+def test_tolerance_mfma_closed_form():
+    assert ogemm.tolerance_mfma(0.0, 0.0) == 1e-6
+    assert ogemm.tolerance_mfma(1e5, 2.0 ** 9) == pytest.approx(1.0 + 1.0 + 1e-6)

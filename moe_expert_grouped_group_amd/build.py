@@ -33,7 +33,8 @@ def _hipcc():
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+            "-Wno-unused-command-line-argument", "-Wno-inline-asm",
+            "-I", os.path.join(ROOT, "include")]
 
 
 def build(verbose=False):

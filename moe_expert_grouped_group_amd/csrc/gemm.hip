@@ -23,23 +23,40 @@
 // inside every workgroup: no host synchronisation, and an expert with no
 // tokens owns no forward/dgrad tile and a zero wgrad output.
 //
-// The MFMA used is V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both operands in
-// E4M3: per lane 32 contraction bytes of one row (two 16-byte runs, see the
-// fragment loads), one E8M0 scale per lane (one 32-element block of the
-// row), fp32 accumulators.
+// Kernel structure (one 256 x 256 output tile per workgroup, 4 waves of
+// 128 x 128):
+//  * MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4, both operands E4M3.  Lane l
+//    (row l % 32 of the operand, half g = l / 32) supplies the contraction
+//    bytes [16g, 16g+16) and [32+16g, 32+16g+16) of a 64-byte step, and the
+//    E8M0 scale of 32-element block g of its row.  Output: lane l holds
+//    column l % 32, rows 8(r/4) + 4(l/32) + r%4 for accumulator r.
+//  * The MFMA's first operand is the B tile and its second the A tile, so a
+//    lane ends with 4 consecutive output columns of one output row.
+//  * Stages of 64 contraction bytes go HBM/L2 -> LDS by LDS DMA (no register
+//    staging) into a ring of 4 buffers, so three stages are in flight while
+//    one is consumed.  Each wave copies a quarter of every stage; a stage is
+//    read only after every wave has waited for its own copies and passed a
+//    barrier.
+//  * Inside a step, the next A fragment is read while the current one's 4
+//    MFMAs run; the barrier sits before the last MFMA group so that the next
+//    stage's B fragments are read while that group runs.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "kernels.h"
 
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;        // output rows per workgroup tile
-constexpr int BN = 128;        // output columns per workgroup tile
-constexpr int BK = 128;        // contraction bytes per stage
-constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 64 x 64
+constexpr int BM = 256;        // output rows per workgroup tile
+constexpr int BN = 256;        // output columns per workgroup tile
+constexpr int BK = 64;         // contraction bytes per stage (one MFMA step)
+constexpr int kStages = 4;     // LDS ring depth
+constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 128 x 128
+constexpr int WT = 128;        // wave tile edge
 constexpr int kMaxGroups = 1024;
 
 struct GemmArgs {
@@ -53,257 +70,421 @@ struct GemmArgs {
   int64_t c_gstride;                   // per-expert offset of C in elements (K-grouped)
   int64_t rows;                        // M-grouped: T; K-grouped: rows of A
   int64_t cols;                        // columns of C
-  int64_t kc;                          // contraction length (M-grouped)
+  int64_t kc;                          // contraction length (M-grouped); T (K-grouped)
   const int64_t* m_splits;
   int32_t G;
   int32_t ntiles_n;                    // cols / BN
-  int32_t ntiles_m;                    // K-grouped: rows / BM
+  int32_t band;                        // K-grouped: row tiles per expert (rows / BM)
+  int32_t ntiles;                      // K-grouped: G * band * ntiles_n tiles
 };
 
-// Exclusive scan over the experts, done by the whole workgroup: finds the
-// expert that owns `target` in the running count of units(g) (tiles or
-// experts), and returns (g, row offset o_g, M_g, target - first unit of g).
-struct GroupHit {
-  int32_t g;
-  int32_t local;
-  int64_t off;
-  int64_t len;
+// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK] (16-byte chunks
+// XOR-swizzled with (row >> 1) & 3, so that the 8 rows of a fragment read
+// that the LDS serves together hit distinct banks), then the scale tiles
+// [BM][4] and [BN][4]: the aligned 4-byte word of E8M0 blocks that holds the
+// stage's two blocks (bytes 2 (kt & 1) and 2 (kt & 1) + 1).
+constexpr int kTileBytesA = BM * BK;
+constexpr int kTileBytesB = BN * BK;
+constexpr int kOffB = kTileBytesA;
+constexpr int kOffSA = kTileBytesA + kTileBytesB;
+constexpr int kOffSB = kOffSA + BM * 4;
+constexpr int kStageBytes = kOffSB + BN * 4;
+constexpr int kDmaPerStage = 10;   // per wave: 4 (A) + 4 (B) + 1 + 1 (scales)
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
+
+// Global -> LDS copies (LDS DMA) from a scalar base address plus a per-lane
+// 32-bit offset (the scalar-base form streams several times faster than one
+// 64-bit address per lane).  Lane i of the wave writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16) (dma16) or [lds + 4 i, lds + 4 i + 4) (dma4);
+// `lds` is a wave-uniform LDS byte address (it goes to M0), passed as an
+// integer so that no generic pointer to LDS has to be formed.  They are issued as inline asm so
+// that the compiler's LDS wait-count tracking covers only the fragment reads
+// (with LDS DMA it can see, it falls back to waiting for every outstanding
+// LDS read before each MFMA group, which serialises the fragment prefetch).
+// Ordering is kept by construction: volatile asm is not moved across the
+// barriers, the explicit s_waitcnt vmcnt that precedes every read of a stage
+// the DMA filled, or the scheduling barriers around the issue block; the
+// copies complete in order with the compiler's own loads, so its vmcnt waits
+// stay conservative.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+               : "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+               : "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q) {
+  const uint64_t v = (uint64_t)(uintptr_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Wait until this wave's copies of the needed stage have landed, given that
+// `later` stages were issued after it (at most kStages - 2 = 2 here).
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaPerStage));
+  } else if (later == 1) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerStage));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
+  const u32x4 x0 = *reinterpret_cast<const u32x4*>(tile + swz(row, g));
+  const u32x4 x1 = *reinterpret_cast<const u32x4*>(tile + swz(row, 2 + g));
+  return __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Expert table kept in LDS for the whole launch: exclusive prefix of tiles
+// (forward/dgrad: ceil(M_g / BM) row tiles per expert) and of token rows, and
+// (wgrad) the experts in decreasing order of tokens.
+struct ExpertTable {
+  int32_t tpre[kMaxGroups + 1];
+  int64_t roff[kMaxGroups + 1];
+  int16_t order[kMaxGroups];
 };
 
-template <bool TILES>
-__device__ GroupHit find_group(const int64_t* __restrict__ m_splits, int G, int64_t target,
-                               int64_t* s_units, int64_t* s_rows, GroupHit* s_hit) {
+// Builds the table with the whole workgroup (4 experts per thread, then a
+// Hillis-Steele scan over the 256 per-thread sums in `scratch`).
+template <bool KGROUPED>
+__device__ void build_table(const int64_t* __restrict__ m_splits, int G, ExpertTable* t,
+                            int64_t* scratch) {
   const int tid = threadIdx.x;
-  constexpr int per = kMaxGroups / kThreads;  // 4 experts per thread
+  constexpr int per = kMaxGroups / kThreads;
   int64_t mv[per];
-  int64_t u_sum = 0, r_sum = 0;
+  int64_t r_sum = 0;
+  int32_t u_sum = 0;
 #pragma unroll
   for (int i = 0; i < per; ++i) {
     const int g = tid * per + i;
     mv[i] = g < G ? max(m_splits[g], (int64_t)0) : 0;   // negative splits count as empty
     r_sum += mv[i];
-    u_sum += TILES ? (mv[i] + BM - 1) / BM : 1;
+    u_sum += (int32_t)((mv[i] + BM - 1) / BM);
   }
-  s_units[tid] = u_sum;
+  int64_t* s_rows = scratch;
+  int64_t* s_units = scratch + kThreads;
   s_rows[tid] = r_sum;
-  if (tid == 0) s_hit->g = -1;
+  s_units[tid] = u_sum;
   __syncthreads();
-  // Hillis-Steele inclusive scan of 256 pairs
   for (int d = 1; d < kThreads; d <<= 1) {
-    int64_t u = 0, r = 0;
+    int64_t r = 0, u = 0;
     if (tid >= d) {
-      u = s_units[tid - d];
       r = s_rows[tid - d];
+      u = s_units[tid - d];
     }
     __syncthreads();
-    s_units[tid] += u;
     s_rows[tid] += r;
+    s_units[tid] += u;
     __syncthreads();
   }
-  int64_t u0 = s_units[tid] - u_sum;   // exclusive prefix
   int64_t r0 = s_rows[tid] - r_sum;
+  int32_t u0 = (int32_t)(s_units[tid] - u_sum);
 #pragma unroll
   for (int i = 0; i < per; ++i) {
     const int g = tid * per + i;
-    const int64_t nu = g < G ? (TILES ? (mv[i] + BM - 1) / BM : 1) : 0;
-    if (g < G && target >= u0 && target < u0 + nu) {
-      s_hit->g = g;
-      s_hit->local = (int32_t)(target - u0);
-      s_hit->off = r0;
-      s_hit->len = mv[i];
+    if (g <= G) {
+      t->roff[g] = r0;
+      t->tpre[g] = u0;
     }
-    u0 += nu;
     r0 += mv[i];
+    u0 += (int32_t)((mv[i] + BM - 1) / BM);
+  }
+  if (tid == kThreads - 1) {   // totals (entry G, also when G == kMaxGroups)
+    t->roff[G] = s_rows[tid];
+    t->tpre[G] = (int32_t)s_units[tid];
   }
   __syncthreads();
-  GroupHit h = *s_hit;
+  if (KGROUPED) {
+    // rank = number of experts with more tokens (ties: lower index first)
+    for (int g = tid; g < G; g += kThreads) {
+      const int64_t mg = t->roff[g + 1] - t->roff[g];
+      int rank = 0;
+      for (int h = 0; h < G; ++h) {
+        const int64_t mh = t->roff[h + 1] - t->roff[h];
+        rank += (mh > mg) || (mh == mg && h < g);
+      }
+      t->order[rank] = (int16_t)g;
+    }
+  }
   __syncthreads();
-  return h;
 }
 
-// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK] (16-byte chunks
-// XOR-swizzled by row so that the 16 rows read by one MFMA operand load hit
-// distinct banks), then the scale tiles [BM][4] and [BN][4].
-constexpr int kTileBytes = BM * BK;
-constexpr int kStageBytes = 2 * kTileBytes + (BM + BN) * 4;
+// One tile's operands.
+struct TileDesc {
+  const uint8_t* a;    // A rows of the tile at contraction 0
+  const uint8_t* sa;
+  const uint8_t* b;
+  const uint8_t* sb;
+  char* c;             // C[m0][n0]
+  int32_t nk;          // contraction steps (BK bytes each)
+  int32_t valid_rows;  // rows of A / C that belong to the tile
+};
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+template <bool KGROUPED>
+__device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTable* t, int tile,
+                                             int64_t esz) {
+  TileDesc d;
+  if (!KGROUPED) {
+    const int mt = tile / p.ntiles_n, nt = tile % p.ntiles_n;
+    // expert g: the last with tpre[g] <= mt (binary search over G + 1 entries)
+    int lo = 0, hi = p.G;                    // tpre[lo] <= mt < tpre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (t->tpre[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int64_t m0 = t->roff[g] + (int64_t)(mt - t->tpre[g]) * BM;
+    const int64_t n0 = (int64_t)nt * BN;
+    const int64_t end = min(t->roff[g + 1], p.rows);   // never past the token count
+    d.valid_rows = (int32_t)max(min((int64_t)BM, end - m0), (int64_t)0);
+    d.a = p.a + m0 * p.lda;
+    d.sa = p.sa + m0 * p.ldsa;
+    d.b = p.b + g * p.b_gstride + n0 * p.ldb;
+    d.sb = p.sb + g * p.sb_gstride + n0 * p.ldsb;
+    d.nk = d.valid_rows > 0 ? (int32_t)(p.kc / BK) : 0;
+    d.c = reinterpret_cast<char*>(p.c) + (m0 * p.ldc + n0) * esz;
+  } else {
+    const int per_expert = p.band * p.ntiles_n;
+    const int g = t->order[tile / per_expert];
+    const int rem = tile % per_expert;
+    const int mtl = rem / p.ntiles_n, nt = rem % p.ntiles_n;
+    const int64_t off = min(t->roff[g], p.kc);            // p.kc = T here
+    const int64_t len = min(t->roff[g + 1], p.kc) - off;
+    const int64_t m0 = (int64_t)mtl * BM, n0 = (int64_t)nt * BN;
+    d.valid_rows = BM;
+    d.a = p.a + m0 * p.lda + off;
+    d.sa = p.sa + m0 * p.ldsa + off / 32;
+    d.b = p.b + n0 * p.ldb + off;
+    d.sb = p.sb + n0 * p.ldsb + off / 32;
+    d.nk = (int32_t)(len / BK);
+    d.c = reinterpret_cast<char*>(p.c) + (g * p.c_gstride + m0 * p.ldc + n0) * esz;
+  }
+  // every lane computed the same values: keep them in scalar registers
+  d.a = uniform_ptr(d.a);
+  d.sa = uniform_ptr(d.sa);
+  d.b = uniform_ptr(d.b);
+  d.sb = uniform_ptr(d.sb);
+  d.c = (char*)uniform_ptr((const uint8_t*)d.c);
+  d.nk = __builtin_amdgcn_readfirstlane(d.nk);
+  d.valid_rows = __builtin_amdgcn_readfirstlane(d.valid_rows);
+  return d;
+}
 
 template <bool KGROUPED, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  __shared__ ExpertTable table;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- tile -> (expert, output block, operand pointers) -------------------
-  int64_t* s_units = reinterpret_cast<int64_t*>(smem);
-  int64_t* s_rows = s_units + kThreads;
-  GroupHit* s_hit = reinterpret_cast<GroupHit*>(s_rows + kThreads);
-
-  const uint8_t *a_base, *sa_base, *b_base, *sb_base;
-  int64_t klen, m0, n0, valid_rows;
-  char* c_base;
   const int64_t esz = OUT_BF16 ? 2 : 4;
-  if (!KGROUPED) {
-    const int nt = blockIdx.x % p.ntiles_n;
-    const int64_t mt = blockIdx.x / p.ntiles_n;
-    const GroupHit h = find_group<true>(p.m_splits, p.G, mt, s_units, s_rows, s_hit);
-    if (h.g < 0) return;                        // beyond the last expert's tiles
-    m0 = h.off + (int64_t)h.local * BM;
-    n0 = (int64_t)nt * BN;
-    // rows of the expert, never past the token count (splits that break the
-    // contract must not make the kernel read or write out of bounds)
-    valid_rows = min(min((int64_t)BM, h.off + h.len - m0), p.rows - m0);
-    if (valid_rows <= 0) return;
-    a_base = p.a + m0 * p.lda;
-    sa_base = p.sa + m0 * p.ldsa;
-    b_base = p.b + h.g * p.b_gstride + n0 * p.ldb;
-    sb_base = p.sb + h.g * p.sb_gstride + n0 * p.ldsb;
-    klen = p.kc;
-    c_base = reinterpret_cast<char*>(p.c) + (m0 * p.ldc + n0) * esz;
-  } else {
-    const int per_group = p.ntiles_m * p.ntiles_n;
-    const int gi = blockIdx.x / per_group;
-    const int rem = blockIdx.x % per_group;
-    const int mt = rem / p.ntiles_n, nt = rem % p.ntiles_n;
-    const GroupHit h = find_group<false>(p.m_splits, p.G, gi, s_units, s_rows, s_hit);
-    m0 = (int64_t)mt * BM;
-    n0 = (int64_t)nt * BN;
-    valid_rows = BM;
-    a_base = p.a + m0 * p.lda + h.off;
-    sa_base = p.sa + m0 * p.ldsa + h.off / 32;
-    b_base = p.b + n0 * p.ldb + h.off;
-    sb_base = p.sb + n0 * p.ldsb + h.off / 32;
-    klen = h.off < p.kc ? min(h.len, p.kc - h.off) : 0;   // p.kc = T here
-    c_base = reinterpret_cast<char*>(p.c) + (h.g * p.c_gstride + m0 * p.ldc + n0) * esz;
-  }
 
-  v4f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the stage buffers serve as scan scratch before any copy is in flight
+  build_table<KGROUPED>(p.m_splits, p.G, &table, reinterpret_cast<int64_t*>(smem));
+  const int ntiles = __builtin_amdgcn_readfirstlane(KGROUPED ? p.ntiles : table.tpre[p.G] * p.ntiles_n);
 
-  // ---- global -> register staging: 4 chunks of A and 4 of B per thread ----
-  // chunk idx = tid + 256 j: row idx/8, 16-byte chunk idx%8 of the row
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
-  int lo[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int idx = tid + kThreads * j;
-    const int r = idx >> 3, ch = idx & 7;
-    const int ra = r < valid_rows ? r : 0;     // rows past the expert: any valid row
-    ga[j] = a_base + ra * p.lda + ch * 16;
-    gb[j] = b_base + r * p.ldb + ch * 16;
-    lo[j] = swz(r, ch);
-  }
-  // scales: threads 0..127 fetch A rows' 4 bytes, 128..255 B rows' 4 bytes
-  const uint8_t* gs;
-  int ls;
-  if (tid < BM) {
-    const int r = tid < valid_rows ? tid : 0;
-    gs = sa_base + r * p.ldsa;
-    ls = 2 * kTileBytes + tid * 4;
-  } else {
-    gs = sb_base + (tid - BM) * p.ldsb;
-    ls = 2 * kTileBytes + BM * 4 + (tid - BM) * 4;
-  }
+  // per-lane DMA geometry: wave w copies rows [64 w, 64 w + 64) of the A and
+  // B tiles, 16 rows (1 KB) per instruction: lane i -> row 16 j + i/4, LDS
+  // chunk slot i%4, which holds global chunk (i%4) ^ ((row >> 1) & 3); and
+  // rows [64 w, 64 w + 64) of both scale tiles, one aligned 4-byte word (4
+  // blocks = two stages) per row.
+  const int dr = lane >> 2;
+  const int dchunk = (lane & 3) ^ ((dr >> 1) & 3);
+  const int srow = wave * 64 + lane;
+  const int fr = lane & 31;   // operand row within a 32-row fragment
+  const int fg = lane >> 5;   // contraction half of the lane
 
-  const int nk = (int)(klen / BK);
-  u32x4 ra[4], rb[4];
-  uint32_t rs = 0;
-  // fragment addresses: operand row (l % 16) of a 16-row sub-tile.  The
-  // instruction takes, in lane l with q = l/16, the contraction bytes
-  // [16q, 16q+16) in its first 16 bytes and [64+16q, 64+16q+16) in its last
-  // 16 (16-byte chunks q and 4+q of the 128-byte stage); the lane's scale
-  // byte is that of 32-element block q of its row.
-  const int fr = lane & 15;
-  const int fq = lane >> 4;
-
-#define MX_GLOAD1(j, kb)                                                  \
-  ra[j] = *reinterpret_cast<const u32x4*>(ga[j] + (kb));                  \
-  rb[j] = *reinterpret_cast<const u32x4*>(gb[j] + (kb));
-#define MX_GLOAD(kt)                                                      \
-  do {                                                                    \
-    const int64_t kb_ = (int64_t)(kt) * BK;                               \
-    MX_GLOAD1(0, kb_) MX_GLOAD1(1, kb_) MX_GLOAD1(2, kb_) MX_GLOAD1(3, kb_) \
-    rs = *reinterpret_cast<const uint32_t*>(gs + kb_ / 32);               \
-  } while (0)
-#define MX_LSTORE1(j, base)                                               \
-  *reinterpret_cast<u32x4*>((base) + lo[j]) = ra[j];                      \
-  *reinterpret_cast<u32x4*>((base) + kTileBytes + lo[j]) = rb[j];
-#define MX_LSTORE(stage)                                                  \
-  do {                                                                    \
-    uint8_t* base_ = smem + (stage) * kStageBytes;                        \
-    MX_LSTORE1(0, base_) MX_LSTORE1(1, base_) MX_LSTORE1(2, base_)        \
-    MX_LSTORE1(3, base_)                                                  \
-    *reinterpret_cast<uint32_t*>(base_ + ls) = rs;                        \
-  } while (0)
-
-  if (nk > 0) {
-    MX_GLOAD(0);
-    MX_LSTORE(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MX_GLOAD(kt + 1);
-    const uint8_t* base = smem + cur * kStageBytes;
-    v8i af[4], bf[4];
-    int as[4], bs[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + fr;
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + swz(r, fq));
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + swz(r, 4 + fq));
-      af[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      as[i] = base[2 * kTileBytes + r * 4 + fq];
-    }
+  uint32_t va[4], vb[4], vsa, vsb;
+  const uint8_t *a_base, *b_base, *sa_base, *sb_base;
+  auto setup = [&](const TileDesc& d) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + fr;
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, fq));
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + kTileBytes + swz(r, 4 + fq));
-      bf[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      bs[j] = base[2 * kTileBytes + BM * 4 + r * 4 + fq];
+      const int r = wave * 64 + j * 16 + dr;
+      const int ra = r < d.valid_rows ? r : 0;   // rows past the expert: any valid row
+      va[j] = (uint32_t)(ra * p.lda + dchunk * 16);
+      vb[j] = (uint32_t)(r * p.ldb + dchunk * 16);
     }
-    // D[n][m] = sum_k B[n,k] A[m,k]: srcA = B fragment, srcB = A fragment, so
-    // each lane ends with 4 consecutive output columns of one output row.
+    vsa = (uint32_t)((srow < d.valid_rows ? srow : 0) * p.ldsa);
+    vsb = (uint32_t)(srow * p.ldsb);
+    a_base = uniform_ptr(d.a);
+    b_base = uniform_ptr(d.b);
+    sa_base = uniform_ptr(d.sa);
+    sb_base = uniform_ptr(d.sb);
+  };
+  // LDS byte address of the stage ring (the low half of the generic address
+  // of an LDS object is its LDS address)
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t kb = (int64_t)kt * BK;
+    const uint32_t base = lds_ring + (uint32_t)((kt % kStages) * kStageBytes);
+    const uint8_t* ak = a_base + kb;
+    const uint8_t* bk = b_base + kb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dma16(ak, va[j], base + (wave * 64 + j * 16) * BK);
+      dma16(bk, vb[j], base + kOffB + (wave * 64 + j * 16) * BK);
+    }
+    dma4(sa_base + (kb >> 7) * 4, vsa, base + kOffSA + wave * 64 * 4);
+    dma4(sb_base + (kb >> 7) * 4, vsb, base + kOffSB + wave * 64 * 4);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  v16f acc[4][4];
+  v8i bf[2][4];
+  int bs[2][4];
+  v8i af[2];
+  int as[2];
+  auto load_b = [&](int kt, int set) {
+    const uint8_t* base = smem + (kt % kStages) * kStageBytes;
+    const int sbyte = 2 * (kt & 1) + fg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * WT + j * 32 + fr;
+      bf[set][j] = frag(base + kOffB, r, fg);
+      bs[set][j] = base[kOffSB + r * 4 + sbyte];
+    }
+  };
+  auto load_a = [&](int kt, int i, int slot) {
+    const uint8_t* base = smem + (kt % kStages) * kStageBytes;
+    const int r = wm * WT + i * 32 + fr;
+    af[slot] = frag(base, r, fg);
+    as[slot] = base[kOffSA + r * 4 + 2 * (kt & 1) + fg];
+  };
+
+  int tile = blockIdx.x;
+  if (tile >= ntiles) return;
+  TileDesc cur = describe<KGROUPED>(p, &table, tile, esz);
+  setup(cur);
+  for (int s = 0; s < kStages; ++s)
+    if (s < cur.nk) issue(s);
+
+  for (;;) {
+    const int nk = cur.nk;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0,
-                                                                     0, 0, bs[j], 0, as[i]);
-    if (kt + 1 < nk) MX_LSTORE(cur ^ 1);
-    __syncthreads();
-  }
-#undef MX_GLOAD
-#undef MX_GLOAD1
-#undef MX_LSTORE
-#undef MX_LSTORE1
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // ---- epilogue: lane holds C[m0 + .. + l%16][n0 + .. + 4(l/16) + 0..3] ----
+    if (nk > 0) {
+      // stage 0 of this tile: its copies were issued before any later copy
+      // or store of this wave, so waiting with at most 2 later stages
+      // outstanding (or none) is enough
+      wait_stage(min(nk - 1, 2));
+      __syncthreads();
+      load_b(0, 0);
+      load_a(0, 0, 0);
+    }
+
+    // D[n][m] = sum_k B[n,k] A[m,k]: srcA = B fragment, srcB = A fragment.
+#define MX_GROUP(I, SET, SLOT)                                                             \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[I][j] =                                \
+      __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[SET][j], af[SLOT], acc[I][j], 0,  \
+                                                      0, 0, bs[SET][j], 0, as[SLOT]);
+
+    // One step: on entry the fragments of stage kt are in (bf[SET], af[0]);
+    // on exit those of stage kt+1 are in (bf[SET^1], af[0]).  Before the last
+    // MFMA group: wait for the LDS reads of stage kt (lgkmcnt(0)), for this
+    // wave's copies of stage kt+1, then the barrier makes stage kt+1 visible
+    // to every wave and frees buffer kt % kStages for stage kt + kStages.
+#define MX_STEP(KT, SET)                                                                   \
+  {                                                                                        \
+    const int kt_ = (KT);                                                                  \
+    load_a(kt_, 1, 1);                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MX_GROUP(0, SET, 0)                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    load_a(kt_, 2, 0);                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MX_GROUP(1, SET, 1)                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    load_a(kt_, 3, 1);                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MX_GROUP(2, SET, 0)                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (kt_ + 1 < nk) {                                                                    \
+      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                 \
+      wait_stage(min(nk - 2 - kt_, kStages - 2));                                          \
+      __syncthreads();                                                                     \
+      if (kt_ + kStages < nk) issue(kt_ + kStages);                                        \
+      load_b(kt_ + 1, (SET) ^ 1);                                                          \
+      load_a(kt_ + 1, 0, 0);                                                               \
+    }                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MX_GROUP(3, SET, 1)                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+  }
+
+    for (int kt = 0; kt < nk; kt += 2) {
+      MX_STEP(kt, 0)
+      MX_STEP(kt + 1, 1)
+    }
+#undef MX_STEP
+#undef MX_GROUP
+
+    // Next tile: once every wave has read the last stage (lgkmcnt(0) + the
+    // barrier), all LDS buffers are free, so its first stages are copied
+    // while this tile's results are stored.
+    const int next = tile + gridDim.x;
+    TileDesc nxt;
+    nxt.nk = 0;
+    if (next < ntiles) {
+      nxt = describe<KGROUPED>(p, &table, next, esz);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __syncthreads();
+      setup(nxt);
+      for (int s = 0; s < kStages; ++s)
+        if (s < nxt.nk) issue(s);
+    }
+
+    // ---- epilogue: lane holds C[m0 + .. + l%32][n0 + .. + 8q + 4(l/32) + 0..3] ----
+    // one per-lane row pointer per tile; the rest are small constant offsets
+    {
+      const int64_t ldc_b = p.ldc * esz;
+      char* lane_c = cur.c + (int64_t)(wm * WT + fr) * ldc_b + (wn * WT + 4 * fg) * esz;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 64 + i * 16 + fr;
-    if (r >= valid_rows) continue;
+      for (int i = 0; i < 4; ++i) {
+        if (wm * WT + i * 32 + fr >= cur.valid_rows) continue;
+        char* row_c = lane_c + (int64_t)(i * 32) * ldc_b;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cidx = wn * 64 + j * 16 + 4 * fq;
-      char* dst = c_base + ((int64_t)r * p.ldc + cidx) * esz;
-      const v4f v = acc[i][j];
-      if (OUT_BF16) {
-        const uint32_t lo2 = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-        const uint32_t hi2 = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            char* dst = row_c + (j * 32 + 8 * q) * esz;
+            const v16f& v = acc[i][j];
+            if (OUT_BF16) {
+              const uint32_t lo2 = f32_to_bf16(v[4 * q]) | (f32_to_bf16(v[4 * q + 1]) << 16);
+              const uint32_t hi2 =
+                  f32_to_bf16(v[4 * q + 2]) | (f32_to_bf16(v[4 * q + 3]) << 16);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
+            } else {
+              *reinterpret_cast<float4*>(dst) =
+                  make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            }
+          }
+        }
       }
     }
+    if (next >= ntiles) break;
+    tile = next;
+    cur = nxt;
   }
 }
 
@@ -325,7 +506,6 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
   p.m_splits = m_splits;
   p.G = G;
   bool kgrouped = false;
-  unsigned grid = 0;
   if (layout == 0) {           // forward: C[T,N] = X[T,K] W_g[N,K]^T
     p.lda = K; p.ldsa = K / 32;
     p.ldb = K; p.ldsb = K / 32;
@@ -344,15 +524,23 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
     p.rows = N; p.cols = K; p.kc = T;
   }
   p.ntiles_n = (int32_t)(p.cols / BN);
+  int64_t upper;
   if (!kgrouped) {
-    // upper bound of sum_g ceil(M_g / BM): T / BM full tiles plus one partial per expert
-    const int64_t mt = T / BM + G;
-    grid = (unsigned)(mt * p.ntiles_n);
+    // at most T / BM full row tiles plus one partial tile per expert
+    upper = (T / BM + G) * p.ntiles_n;
   } else {
-    p.ntiles_m = (int32_t)(p.rows / BM);
-    grid = (unsigned)((int64_t)G * p.ntiles_m * p.ntiles_n);
+    p.band = (int32_t)(p.rows / BM);
+    p.ntiles = G * p.band * p.ntiles_n;
+    upper = p.ntiles;
   }
-  if (kgrouped) return out_bf16 ? launch_one<true, true>(p, grid, st) : launch_one<true, false>(p, grid, st);
+  // persistent grid: one workgroup per CU (the LDS ring allows one), each
+  // walking the tiles with a stride of the grid size
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+  if (kgrouped)
+    return out_bf16 ? launch_one<true, true>(p, grid, st) : launch_one<true, false>(p, grid, st);
   return out_bf16 ? launch_one<false, true>(p, grid, st) : launch_one<false, false>(p, grid, st);
 }
 

@@ -80,16 +80,22 @@ struct GemmArgs {
 
 // LDS layout of one stage: A tile [BM][BK], B tile [BN][BK] (16-byte chunks
 // XOR-swizzled with (row >> 1) & 3, so that the 8 rows of a fragment read
-// that the LDS serves together hit distinct banks), then the scale tiles
-// [BM][4] and [BN][4]: the aligned 4-byte word of E8M0 blocks that holds the
-// stage's two blocks (bytes 2 (kt & 1) and 2 (kt & 1) + 1).
+// that the LDS serves together hit distinct banks).
 constexpr int kTileBytesA = BM * BK;
 constexpr int kTileBytesB = BN * BK;
 constexpr int kOffB = kTileBytesA;
-constexpr int kOffSA = kTileBytesA + kTileBytesB;
-constexpr int kOffSB = kOffSA + BM * 4;
-constexpr int kStageBytes = kOffSB + BN * 4;
-constexpr int kDmaPerStage = 10;   // per wave: 4 (A) + 4 (B) + 1 + 1 (scales)
+constexpr int kStageBytes = kTileBytesA + kTileBytesB;
+constexpr int kDmaPerStage = 8;    // per wave: 4 (A) + 4 (B) data copies
+// E8M0 scales arrive in groups of kScaleSteps stages: 16 bytes (16 blocks of
+// 32) per operand row, [BM][16] for A then [BN][16] for B, double-buffered.
+// Copying a row's scale bytes one stage at a time would cost one cache-line
+// request per row per stage for 2 bytes of data, as many requests as the
+// operand tiles themselves.
+constexpr int kScaleSteps = 8;
+constexpr int kScaleRow = 2 * kScaleSteps;   // bytes per row and group
+constexpr int kScOffB = BM * kScaleRow;
+constexpr int kScaleBuf = (BM + BN) * kScaleRow;
+constexpr int kScaleDma = 8;       // per wave and group: 4 (A) + 4 (B), 16 rows each
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 1) & 3)) << 4);
@@ -132,7 +138,10 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q) {
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Wait until this wave's copies of the needed stage have landed, given that
-// `later` stages were issued after it (at most kStages - 2 = 2 here).
+// `later` stages were issued after it (at most kStages - 2 = 2 here).  A
+// stage that opens a scale group carries kScaleDma more copies; counting only
+// the kDmaPerStage data copies of the later stages waits for at least as many
+// completions as needed (copies complete in issue order).
 __device__ __forceinline__ void wait_stage(int later) {
   if (later >= 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaPerStage));
@@ -232,6 +241,7 @@ struct TileDesc {
   char* c;             // C[m0][n0]
   int32_t nk;          // contraction steps (BK bytes each)
   int32_t valid_rows;  // rows of A / C that belong to the tile
+  int32_t nblk;        // scale blocks of the tile's contraction (nk * 2)
 };
 
 template <bool KGROUPED>
@@ -256,14 +266,17 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.b = p.b + g * p.b_gstride + n0 * p.ldb;
     d.sb = p.sb + g * p.sb_gstride + n0 * p.ldsb;
     d.nk = d.valid_rows > 0 ? (int32_t)(p.kc / BK) : 0;
+    d.nblk = (int32_t)(p.kc / 32);
     d.c = reinterpret_cast<char*>(p.c) + (m0 * p.ldc + n0) * esz;
   } else {
     const int per_expert = p.band * p.ntiles_n;
     const int g = t->order[tile / per_expert];
     const int rem = tile % per_expert;
     const int mtl = rem / p.ntiles_n, nt = rem % p.ntiles_n;
-    const int64_t off = min(t->roff[g], p.kc);            // p.kc = T here
-    const int64_t len = min(t->roff[g + 1], p.kc) - off;
+    // p.kc = T here.  Runs are multiples of 128 tokens by contract; rounding
+    // down keeps every copy inside [0, T) and aligned for any split values.
+    const int64_t off = min(t->roff[g], p.kc) & ~(int64_t)127;
+    const int64_t len = max(min(t->roff[g + 1], p.kc) - off, (int64_t)0) & ~(int64_t)127;
     const int64_t m0 = (int64_t)mtl * BM, n0 = (int64_t)nt * BN;
     d.valid_rows = BM;
     d.a = p.a + m0 * p.lda + off;
@@ -271,6 +284,7 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.b = p.b + n0 * p.ldb + off;
     d.sb = p.sb + n0 * p.ldsb + off / 32;
     d.nk = (int32_t)(len / BK);
+    d.nblk = (int32_t)(len / 32);
     d.c = reinterpret_cast<char*>(p.c) + (g * p.c_gstride + m0 * p.ldc + n0) * esz;
   }
   // every lane computed the same values: keep them in scalar registers
@@ -280,13 +294,14 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
   d.sb = uniform_ptr(d.sb);
   d.c = (char*)uniform_ptr((const uint8_t*)d.c);
   d.nk = __builtin_amdgcn_readfirstlane(d.nk);
+  d.nblk = __builtin_amdgcn_readfirstlane(d.nblk);
   d.valid_rows = __builtin_amdgcn_readfirstlane(d.valid_rows);
   return d;
 }
 
 template <bool KGROUPED, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,17 +315,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 
   // per-lane DMA geometry: wave w copies rows [64 w, 64 w + 64) of the A and
   // B tiles, 16 rows (1 KB) per instruction: lane i -> row 16 j + i/4, LDS
-  // chunk slot i%4, which holds global chunk (i%4) ^ ((row >> 1) & 3); and
-  // rows [64 w, 64 w + 64) of both scale tiles, one aligned 4-byte word (4
-  // blocks = two stages) per row.
+  // chunk slot i%4, which holds global chunk (i%4) ^ ((row >> 1) & 3).  The
+  // scale groups use the same rows, 16 rows x 16 bytes per instruction: lane
+  // i -> row 16 j + i/4, bytes 4 (i%4) .. 4 (i%4) + 3 of the row's group.
   const int dr = lane >> 2;
   const int dchunk = (lane & 3) ^ ((dr >> 1) & 3);
-  const int srow = wave * 64 + lane;
+  const int scol = (lane & 3) * 4;
   const int fr = lane & 31;   // operand row within a 32-row fragment
   const int fg = lane >> 5;   // contraction half of the lane
 
-  uint32_t va[4], vb[4], vsa, vsb;
+  uint32_t va[4], vb[4];
   const uint8_t *a_base, *b_base, *sa_base, *sb_base;
+  int s_valid, s_nblk;
   auto setup = [&](const TileDesc& d) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -319,29 +335,50 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       va[j] = (uint32_t)(ra * p.lda + dchunk * 16);
       vb[j] = (uint32_t)(r * p.ldb + dchunk * 16);
     }
-    vsa = (uint32_t)((srow < d.valid_rows ? srow : 0) * p.ldsa);
-    vsb = (uint32_t)(srow * p.ldsb);
     a_base = uniform_ptr(d.a);
     b_base = uniform_ptr(d.b);
     sa_base = uniform_ptr(d.sa);
     sb_base = uniform_ptr(d.sb);
+    s_valid = d.valid_rows;
+    s_nblk = d.nblk;
   };
-  // LDS byte address of the stage ring (the low half of the generic address
-  // of an LDS object is its LDS address)
+  // LDS byte addresses of the stage ring and of the scale buffers (the low
+  // half of the generic address of an LDS object is its LDS address)
   const uint32_t lds_ring = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int kt) {
-    __builtin_amdgcn_sched_barrier(0);
+  const uint32_t lds_sc = lds_ring + kStages * kStageBytes;
+  // Scale group `grp` (blocks [16 grp, 16 grp + 16) of every row) into buffer
+  // grp % 2.  In a K-grouped tile the last group may run past the expert's
+  // blocks (s_nblk, a multiple of 4): those lanes re-read the last valid word.
+  // part j (0..3) of scale group grp: rows 64 w + 16 j .. + 16 of A and of B
+  auto scale_part = [&](int grp, int j) {
+    const uint32_t buf = lds_sc + (uint32_t)((grp & 1) * kScaleBuf);
+    const int col = KGROUPED ? max(min(scol, s_nblk - 4 - 16 * grp), 0) : scol;
+    const int r = wave * 64 + j * 16 + dr;
+    const int ra = r < s_valid ? r : 0;
+    dma4(sa_base + 16 * grp, (uint32_t)(ra * (int)p.ldsa + col),
+         buf + (wave * 64 + j * 16) * kScaleRow);
+    dma4(sb_base + 16 * grp, (uint32_t)(r * (int)p.ldsb + col),
+         buf + kScOffB + (wave * 64 + j * 16) * kScaleRow);
+  };
+  // part q (0..7) of the data copies of stage kt: rows 64 w + 16 (q/2) .. + 16
+  // of A (q even) or B (q odd)
+  auto data_part = [&](int kt, int q) {
     const int64_t kb = (int64_t)kt * BK;
     const uint32_t base = lds_ring + (uint32_t)((kt % kStages) * kStageBytes);
-    const uint8_t* ak = a_base + kb;
-    const uint8_t* bk = b_base + kb;
+    const int j = q >> 1;
+    if ((q & 1) == 0)
+      dma16(a_base + kb, va[j], base + (wave * 64 + j * 16) * BK);
+    else
+      dma16(b_base + kb, vb[j], base + kOffB + (wave * 64 + j * 16) * BK);
+  };
+  // a whole stage at once (first stages of a tile)
+  auto issue = [&](int kt) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dma16(ak, va[j], base + (wave * 64 + j * 16) * BK);
-      dma16(bk, vb[j], base + kOffB + (wave * 64 + j * 16) * BK);
-    }
-    dma4(sa_base + (kb >> 7) * 4, vsa, base + kOffSA + wave * 64 * 4);
-    dma4(sb_base + (kb >> 7) * 4, vsb, base + kOffSB + wave * 64 * 4);
+    for (int q = 0; q < 8; ++q) data_part(kt, q);
+    if (kt % kScaleSteps == 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) scale_part(kt / kScaleSteps, j);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -350,28 +387,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   int bs[2][4];
   v8i af[2];
   int as[2];
-  auto load_b = [&](int kt, int set) {
+  // the scale byte of (row, step kt) for this lane's block half
+  auto scale_at = [&](int kt, int off_row) {
+    const uint8_t* sc = smem + kStages * kStageBytes + ((kt / kScaleSteps) & 1) * kScaleBuf;
+    return (int)sc[off_row * kScaleRow + 2 * (kt % kScaleSteps) + fg];
+  };
+  auto load_b = [&](int kt, int set, int j) {
     const uint8_t* base = smem + (kt % kStages) * kStageBytes;
-    const int sbyte = 2 * (kt & 1) + fg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * WT + j * 32 + fr;
-      bf[set][j] = frag(base + kOffB, r, fg);
-      bs[set][j] = base[kOffSB + r * 4 + sbyte];
-    }
+    const int r = wn * WT + j * 32 + fr;
+    bf[set][j] = frag(base + kOffB, r, fg);
+    bs[set][j] = scale_at(kt, BM + r);
   };
   auto load_a = [&](int kt, int i, int slot) {
     const uint8_t* base = smem + (kt % kStages) * kStageBytes;
     const int r = wm * WT + i * 32 + fr;
     af[slot] = frag(base, r, fg);
-    as[slot] = base[kOffSA + r * 4 + 2 * (kt & 1) + fg];
+    as[slot] = scale_at(kt, r);
   };
 
   int tile = blockIdx.x;
   if (tile >= ntiles) return;
   TileDesc cur = describe<KGROUPED>(p, &table, tile, esz);
   setup(cur);
-  for (int s = 0; s < kStages; ++s)
+  for (int s = 0; s < kStages - 1; ++s)
     if (s < cur.nk) issue(s);
 
   for (;;) {
@@ -389,47 +427,64 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       // outstanding (or none) is enough
       wait_stage(min(nk - 1, 2));
       __syncthreads();
-      load_b(0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_b(0, 0, j);
       load_a(0, 0, 0);
     }
 
     // D[n][m] = sum_k B[n,k] A[m,k]: srcA = B fragment, srcB = A fragment.
-#define MX_GROUP(I, SET, SLOT)                                                             \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[I][j] =                                \
-      __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[SET][j], af[SLOT], acc[I][j], 0,  \
-                                                      0, 0, bs[SET][j], 0, as[SLOT]);
+// The MFMA builtin has no side effects, so without the empty asm that takes
+// its result the compiler may sink it past the uniform branches of the step
+// (a scheduling barrier orders instructions only inside one basic block).
+#define MX_MFMA(I, J, SET, SLOT)                                                            \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[SET][J], af[SLOT], acc[I][J], \
+                                                            0, 0, 0, bs[SET][J], 0, as[SLOT]);   \
+  asm volatile("" : "+a"(acc[I][J]));                                                       \
+  __builtin_amdgcn_sched_barrier(0);
+#define MX_FENCE __builtin_amdgcn_sched_barrier(0);
 
-    // One step: on entry the fragments of stage kt are in (bf[SET], af[0]);
-    // on exit those of stage kt+1 are in (bf[SET^1], af[0]).  Before the last
-    // MFMA group: wait for the LDS reads of stage kt (lgkmcnt(0)), for this
-    // wave's copies of stage kt+1, then the barrier makes stage kt+1 visible
-    // to every wave and frees buffer kt % kStages for stage kt + kStages.
-#define MX_STEP(KT, SET)                                                                   \
-  {                                                                                        \
-    const int kt_ = (KT);                                                                  \
-    load_a(kt_, 1, 1);                                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MX_GROUP(0, SET, 0)                                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    load_a(kt_, 2, 0);                                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MX_GROUP(1, SET, 1)                                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    load_a(kt_, 3, 1);                                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MX_GROUP(2, SET, 0)                                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    if (kt_ + 1 < nk) {                                                                    \
-      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                 \
-      wait_stage(min(nk - 2 - kt_, kStages - 2));                                          \
-      __syncthreads();                                                                     \
-      if (kt_ + kStages < nk) issue(kt_ + kStages);                                        \
-      load_b(kt_ + 1, (SET) ^ 1);                                                          \
-      load_a(kt_ + 1, 0, 0);                                                               \
-    }                                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MX_GROUP(3, SET, 1)                                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
+    // One step (16 MFMAs per wave).  On entry the fragments of stage kt are
+    // in (bf[SET], af[0]); on exit those of stage kt+1 are in (bf[SET^1],
+    // af[0]).  With one wave per SIMD, anything issued between two MFMAs that
+    // takes longer than an MFMA leaves the matrix pipe idle, so the work of a
+    // step is spread one item per MFMA: the A fragment of the next group, the
+    // 8 data copies of stage kt+3 (into the buffer freed by the previous
+    // step's barrier), the scale group that starts at stage kt+3, then after
+    // the barrier the B fragments and first A fragment of stage kt+1.  The
+    // barrier follows this wave's wait for its LDS reads of stage kt and for
+    // its copies of stage kt+1: after it stage kt+1 is visible to every wave
+    // and buffer kt % kStages is free for stage kt+4 (copied in step kt+1).
+#define MX_STEP(KT, SET)                                                                    \
+  {                                                                                         \
+    const int kt_ = (KT);                                                                   \
+    const bool pf_ = kt_ + 3 < nk;                                                          \
+    const bool sg_ = pf_ && ((kt_ + 3) % kScaleSteps == 0);                                 \
+    const bool nx_ = kt_ + 1 < nk;                                                          \
+    const int g_ = (kt_ + 3) / kScaleSteps;                                                 \
+    MX_MFMA(0, 0, SET, 0) load_a(kt_, 1, 1); MX_FENCE                                       \
+    MX_MFMA(0, 1, SET, 0) if (pf_) data_part(kt_ + 3, 0); MX_FENCE                          \
+    MX_MFMA(0, 2, SET, 0) if (pf_) data_part(kt_ + 3, 1); MX_FENCE                          \
+    MX_MFMA(0, 3, SET, 0) if (pf_) data_part(kt_ + 3, 2); MX_FENCE                          \
+    MX_MFMA(1, 0, SET, 1) load_a(kt_, 2, 0); if (pf_) data_part(kt_ + 3, 3); MX_FENCE       \
+    MX_MFMA(1, 1, SET, 1) if (pf_) data_part(kt_ + 3, 4); MX_FENCE                          \
+    MX_MFMA(1, 2, SET, 1) if (pf_) data_part(kt_ + 3, 5); MX_FENCE                          \
+    MX_MFMA(1, 3, SET, 1) if (pf_) data_part(kt_ + 3, 6); MX_FENCE                          \
+    MX_MFMA(2, 0, SET, 0) load_a(kt_, 3, 1); if (pf_) data_part(kt_ + 3, 7); MX_FENCE       \
+    MX_MFMA(2, 1, SET, 0) if (sg_) scale_part(g_, 0); MX_FENCE                              \
+    MX_MFMA(2, 2, SET, 0) if (sg_) scale_part(g_, 1); MX_FENCE                              \
+    MX_MFMA(2, 3, SET, 0) if (sg_) { scale_part(g_, 2); scale_part(g_, 3); }                \
+    if (nx_) {                                                                              \
+      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                  \
+      wait_stage(min(nk - 2 - kt_, kStages - 2));                                           \
+      __syncthreads();                                                                      \
+    }                                                                                       \
+    MX_FENCE                                                                                \
+    MX_MFMA(3, 0, SET, 1) if (nx_) { load_b(kt_ + 1, (SET) ^ 1, 0); load_b(kt_ + 1, (SET) ^ 1, 1); } \
+    MX_FENCE                                                                                \
+    MX_MFMA(3, 1, SET, 1) if (nx_) { load_b(kt_ + 1, (SET) ^ 1, 2); load_b(kt_ + 1, (SET) ^ 1, 3); } \
+    MX_FENCE                                                                                \
+    MX_MFMA(3, 2, SET, 1) if (nx_) load_a(kt_ + 1, 0, 0); MX_FENCE                          \
+    MX_MFMA(3, 3, SET, 1)                                                                   \
   }
 
     for (int kt = 0; kt < nk; kt += 2) {
@@ -437,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       MX_STEP(kt + 1, 1)
     }
 #undef MX_STEP
-#undef MX_GROUP
+#undef MX_FENCE
+#undef MX_MFMA
 
     // Next tile: once every wave has read the last stage (lgkmcnt(0) + the
     // barrier), all LDS buffers are free, so its first stages are copied
@@ -450,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
       setup(nxt);
-      for (int s = 0; s < kStages; ++s)
+      for (int s = 0; s < kStages - 1; ++s)
         if (s < nxt.nk) issue(s);
     }
 

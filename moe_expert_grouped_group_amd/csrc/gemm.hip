@@ -30,8 +30,9 @@
 //    bytes [16g, 16g+16) and [32+16g, 32+16g+16) of a 64-byte step, and the
 //    E8M0 scale of 32-element block g of its row.  Output: lane l holds
 //    column l % 32, rows 8(r/4) + 4(l/32) + r%4 for accumulator r.
-//  * The MFMA's first operand is the B tile and its second the A tile, so a
-//    lane ends with 4 consecutive output columns of one output row.
+//  * The MFMA's first operand is the A tile and its second the B tile, so the
+//    32 lanes of a half-wave hold 32 consecutive output columns of one row:
+//    a store of one accumulator register writes whole cache lines.
 //  * Stages of 64 contraction bytes go HBM/L2 -> LDS by LDS DMA (no register
 //    staging) into a ring of 4 buffers, so three stages are in flight while
 //    one is consumed.  Each wave copies a quarter of every stage; a stage is
@@ -432,13 +433,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       load_a(0, 0, 0);
     }
 
-    // D[n][m] = sum_k B[n,k] A[m,k]: srcA = B fragment, srcB = A fragment.
+    // D[m][n] = sum_k A[m,k] B[n,k]: srcA = A fragment, srcB = B fragment.
 // The MFMA builtin has no side effects, so without the empty asm that takes
 // its result the compiler may sink it past the uniform branches of the step
 // (a scheduling barrier orders instructions only inside one basic block).
 #define MX_MFMA(I, J, SET, SLOT)                                                            \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[SET][J], af[SLOT], acc[I][J], \
-                                                            0, 0, 0, bs[SET][J], 0, as[SLOT]);   \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[SLOT], bf[SET][J], acc[I][J], \
+                                                            0, 0, 0, as[SLOT], 0, bs[SET][J]);   \
   asm volatile("" : "+a"(acc[I][J]));                                                       \
   __builtin_amdgcn_sched_barrier(0);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
@@ -510,30 +511,32 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         if (s < nxt.nk) issue(s);
     }
 
-    // ---- epilogue: lane holds C[m0 + .. + l%32][n0 + .. + 8q + 4(l/32) + 0..3] ----
-    // one per-lane row pointer per tile; the rest are small constant offsets
+    // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
+    // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32,
+    // so one store instruction per register writes 32 consecutive columns of
+    // two rows: whole 128-byte lines for fp32 output.  The row part of the
+    // address is wave-uniform (scalar base); the lane part is a 32-bit offset.
+    // Global (not generic) stores: a generic store also counts on the LDS
+    // wait counter, which the loop waits on for its fragment reads.
     {
       const int64_t ldc_b = p.ldc * esz;
-      char* lane_c = cur.c + (int64_t)(wm * WT + fr) * ldc_b + (wn * WT + 4 * fg) * esz;
+      const int wm_u = __builtin_amdgcn_readfirstlane(wm);
+      const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (int64_t)(wn * WT + fr) * esz);
+      const int vrows = cur.valid_rows;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (wm * WT + i * 32 + fr >= cur.valid_rows) continue;
-        char* row_c = lane_c + (int64_t)(i * 32) * ldc_b;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+          if (vrows < BM && row + 4 * fg >= vrows) continue;
+          char* rbase = cur.c + (int64_t)row * ldc_b + lane_off;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            char* dst = row_c + (j * 32 + 8 * q) * esz;
-            const v16f& v = acc[i][j];
-            if (OUT_BF16) {
-              const uint32_t lo2 = f32_to_bf16(v[4 * q]) | (f32_to_bf16(v[4 * q + 1]) << 16);
-              const uint32_t hi2 =
-                  f32_to_bf16(v[4 * q + 2]) | (f32_to_bf16(v[4 * q + 3]) << 16);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(lo2, hi2);
-            } else {
-              *reinterpret_cast<float4*>(dst) =
-                  make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-            }
+          for (int j = 0; j < 4; ++j) {
+            if (OUT_BF16)
+              *(__attribute__((address_space(1))) uint16_t*)(rbase + j * 32 * 2) =
+                  (uint16_t)f32_to_bf16(acc[i][j][r]);
+            else
+              *(__attribute__((address_space(1))) float*)(rbase + j * 32 * 4) = acc[i][j][r];
           }
         }
       }

@@ -139,12 +139,14 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q) {
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Wait until this wave's copies of the needed stage have landed, given that
-// `later` stages were issued after it (at most kStages - 2 = 2 here).  A
+// `later` stages were issued after it (at most kStages - 1 = 3).  A
 // stage that opens a scale group carries kScaleDma more copies; counting only
 // the kDmaPerStage data copies of the later stages waits for at least as many
 // completions as needed (copies complete in issue order).
 __device__ __forceinline__ void wait_stage(int later) {
-  if (later >= 2) {
+  if (later >= 3) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kDmaPerStage));
+  } else if (later == 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaPerStage));
   } else if (later == 1) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerStage));
@@ -384,11 +386,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   };
 
   v16f acc[4][4];
-  v8i bf[2][4];
-  int bs[2][4];
-  v8i af[2];
-  int as[2];
-  // the scale byte of (row, step kt) for this lane's block half
+  // fragments of two stages: set kt & 1 feeds the MFMAs of step kt while the
+  // other set is filled from stage kt + 1
+  v8i af[2][4], bf[2][4];
+  int as[2][4], bs[2][4];
+  // the scale byte of (row, stage kt) for this lane's block half
   auto scale_at = [&](int kt, int off_row) {
     const uint8_t* sc = smem + kStages * kStageBytes + ((kt / kScaleSteps) & 1) * kScaleBuf;
     return (int)sc[off_row * kScaleRow + 2 * (kt % kScaleSteps) + fg];
@@ -399,18 +401,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     bf[set][j] = frag(base + kOffB, r, fg);
     bs[set][j] = scale_at(kt, BM + r);
   };
-  auto load_a = [&](int kt, int i, int slot) {
+  auto load_a = [&](int kt, int set, int i) {
     const uint8_t* base = smem + (kt % kStages) * kStageBytes;
     const int r = wm * WT + i * 32 + fr;
-    af[slot] = frag(base, r, fg);
-    as[slot] = scale_at(kt, r);
+    af[set][i] = frag(base, r, fg);
+    as[set][i] = scale_at(kt, r);
   };
 
   int tile = blockIdx.x;
   if (tile >= ntiles) return;
   TileDesc cur = describe<KGROUPED>(p, &table, tile, esz);
   setup(cur);
-  for (int s = 0; s < kStages - 1; ++s)
+  for (int s = 0; s < kStages; ++s)
     if (s < cur.nk) issue(s);
 
   for (;;) {
@@ -424,68 +426,67 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 
     if (nk > 0) {
       // stage 0 of this tile: its copies were issued before any later copy
-      // or store of this wave, so waiting with at most 2 later stages
-      // outstanding (or none) is enough
-      wait_stage(min(nk - 1, 2));
+      // or store of this wave, and at most 3 later stages follow them
+      wait_stage(min(nk - 1, 3));
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_b(0, 0, j);
-      load_a(0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        load_a(0, 0, i);
+        load_b(0, 0, i);
+      }
     }
 
     // D[m][n] = sum_k A[m,k] B[n,k]: srcA = A fragment, srcB = B fragment.
 // The MFMA builtin has no side effects, so without the empty asm that takes
 // its result the compiler may sink it past the uniform branches of the step
 // (a scheduling barrier orders instructions only inside one basic block).
-#define MX_MFMA(I, J, SET, SLOT)                                                            \
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[SLOT], bf[SET][J], acc[I][J], \
-                                                            0, 0, 0, as[SLOT], 0, bs[SET][J]);   \
+#define MX_MFMA(I, J, SET)                                                                  \
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                              \
+      af[SET][I], bf[SET][J], acc[I][J], 0, 0, 0, as[SET][I], 0, bs[SET][J]);               \
   asm volatile("" : "+a"(acc[I][J]));                                                       \
   __builtin_amdgcn_sched_barrier(0);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
 
-    // One step (16 MFMAs per wave).  On entry the fragments of stage kt are
-    // in (bf[SET], af[0]); on exit those of stage kt+1 are in (bf[SET^1],
-    // af[0]).  With one wave per SIMD, anything issued between two MFMAs that
-    // takes longer than an MFMA leaves the matrix pipe idle, so the work of a
-    // step is spread one item per MFMA: the A fragment of the next group, the
-    // 8 data copies of stage kt+3 (into the buffer freed by the previous
-    // step's barrier), the scale group that starts at stage kt+3, then after
-    // the barrier the B fragments and first A fragment of stage kt+1.  The
-    // barrier follows this wave's wait for its LDS reads of stage kt and for
-    // its copies of stage kt+1: after it stage kt+1 is visible to every wave
-    // and buffer kt % kStages is free for stage kt+4 (copied in step kt+1).
+    // One step (16 MFMAs per wave) on the fragments of stage kt, held in
+    // registers (set SET) since the previous step.  The step opens with the
+    // only barrier: before it this wave waits for its LDS reads of stage kt
+    // and for its copies of stage kt+1; after it stage kt+1 is visible to
+    // every wave and buffer kt % kStages is free.  The MFMAs then run with
+    // one item of other work after each (with one wave per SIMD, anything
+    // longer between two MFMAs idles the matrix pipe): the reads of stage
+    // kt+1 into the other set, the 8 copies of stage kt+4 into the freed
+    // buffer, and the scale group that starts at stage kt+4.
 #define MX_STEP(KT, SET)                                                                    \
   {                                                                                         \
     const int kt_ = (KT);                                                                   \
-    const bool pf_ = kt_ + 3 < nk;                                                          \
-    const bool sg_ = pf_ && ((kt_ + 3) % kScaleSteps == 0);                                 \
     const bool nx_ = kt_ + 1 < nk;                                                          \
-    const int g_ = (kt_ + 3) / kScaleSteps;                                                 \
-    MX_MFMA(0, 0, SET, 0) load_a(kt_, 1, 1); MX_FENCE                                       \
-    MX_MFMA(0, 1, SET, 0) if (pf_) data_part(kt_ + 3, 0); MX_FENCE                          \
-    MX_MFMA(0, 2, SET, 0) if (pf_) data_part(kt_ + 3, 1); MX_FENCE                          \
-    MX_MFMA(0, 3, SET, 0) if (pf_) data_part(kt_ + 3, 2); MX_FENCE                          \
-    MX_MFMA(1, 0, SET, 1) load_a(kt_, 2, 0); if (pf_) data_part(kt_ + 3, 3); MX_FENCE       \
-    MX_MFMA(1, 1, SET, 1) if (pf_) data_part(kt_ + 3, 4); MX_FENCE                          \
-    MX_MFMA(1, 2, SET, 1) if (pf_) data_part(kt_ + 3, 5); MX_FENCE                          \
-    MX_MFMA(1, 3, SET, 1) if (pf_) data_part(kt_ + 3, 6); MX_FENCE                          \
-    MX_MFMA(2, 0, SET, 0) load_a(kt_, 3, 1); if (pf_) data_part(kt_ + 3, 7); MX_FENCE       \
-    MX_MFMA(2, 1, SET, 0) if (sg_) scale_part(g_, 0); MX_FENCE                              \
-    MX_MFMA(2, 2, SET, 0) if (sg_) scale_part(g_, 1); MX_FENCE                              \
-    MX_MFMA(2, 3, SET, 0) if (sg_) { scale_part(g_, 2); scale_part(g_, 3); }                \
+    const bool pf_ = kt_ + 4 < nk;                                                          \
+    const bool sg_ = pf_ && ((kt_ + 4) % kScaleSteps == 0);                                 \
+    const int g_ = (kt_ + 4) / kScaleSteps;                                                 \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage kt */    \
     if (nx_) {                                                                              \
-      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                                  \
       wait_stage(min(nk - 2 - kt_, kStages - 2));                                           \
       __syncthreads();                                                                      \
     }                                                                                       \
     MX_FENCE                                                                                \
-    MX_MFMA(3, 0, SET, 1) if (nx_) { load_b(kt_ + 1, (SET) ^ 1, 0); load_b(kt_ + 1, (SET) ^ 1, 1); } \
+    MX_MFMA(0, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 0); MX_FENCE                     \
+    MX_MFMA(0, 1, SET) if (pf_) data_part(kt_ + 4, 0); MX_FENCE                             \
+    MX_MFMA(0, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 0); MX_FENCE                     \
+    MX_MFMA(0, 3, SET) if (pf_) data_part(kt_ + 4, 1); MX_FENCE                             \
+    MX_MFMA(1, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 1); MX_FENCE                     \
+    MX_MFMA(1, 1, SET) if (pf_) data_part(kt_ + 4, 2); MX_FENCE                             \
+    MX_MFMA(1, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 1); MX_FENCE                     \
+    MX_MFMA(1, 3, SET) if (pf_) data_part(kt_ + 4, 3); MX_FENCE                             \
+    MX_MFMA(2, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 2); MX_FENCE                     \
+    MX_MFMA(2, 1, SET) if (pf_) data_part(kt_ + 4, 4); MX_FENCE                             \
+    MX_MFMA(2, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 2); MX_FENCE                     \
+    MX_MFMA(2, 3, SET) if (pf_) data_part(kt_ + 4, 5); MX_FENCE                             \
+    MX_MFMA(3, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 3); if (pf_) data_part(kt_ + 4, 6); \
     MX_FENCE                                                                                \
-    MX_MFMA(3, 1, SET, 1) if (nx_) { load_b(kt_ + 1, (SET) ^ 1, 2); load_b(kt_ + 1, (SET) ^ 1, 3); } \
+    MX_MFMA(3, 1, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 3); if (pf_) data_part(kt_ + 4, 7); \
     MX_FENCE                                                                                \
-    MX_MFMA(3, 2, SET, 1) if (nx_) load_a(kt_ + 1, 0, 0); MX_FENCE                          \
-    MX_MFMA(3, 3, SET, 1)                                                                   \
+    MX_MFMA(3, 2, SET) if (sg_) { scale_part(g_, 0); scale_part(g_, 1); } MX_FENCE          \
+    MX_MFMA(3, 3, SET) if (sg_) { scale_part(g_, 2); scale_part(g_, 3); } MX_FENCE          \
   }
 
     for (int kt = 0; kt < nk; kt += 2) {
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
       setup(nxt);
-      for (int s = 0; s < kStages - 1; ++s)
+      for (int s = 0; s < kStages; ++s)
         if (s < nxt.nk) issue(s);
     }
 

@@ -79,9 +79,11 @@ struct GemmArgs {
   int32_t ntiles;                      // K-grouped: G * band * ntiles_n tiles
 };
 
-// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK] (16-byte chunks
-// XOR-swizzled with (row >> 1) & 3, so that the 8 rows of a fragment read
-// that the LDS serves together hit distinct banks).
+// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK], 16-byte chunk c
+// of row r stored at chunk position c ^ ((r >> 1) & 3).  The LDS has 32
+// banks of 4 bytes, so two 64-byte rows share one bank line; the 8
+// consecutive rows of a fragment read that the LDS serves together then use
+// 8 distinct 16-byte bank groups.
 constexpr int kTileBytesA = BM * BK;
 constexpr int kTileBytesB = BN * BK;
 constexpr int kOffB = kTileBytesA;
@@ -97,10 +99,6 @@ constexpr int kScaleRow = 2 * kScaleSteps;   // bytes per row and group
 constexpr int kScOffB = BM * kScaleRow;
 constexpr int kScaleBuf = (BM + BN) * kScaleRow;
 constexpr int kScaleDma = 8;       // per wave and group: 4 (A) + 4 (B), 16 rows each
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 3)) << 4);
-}
 
 // Global -> LDS copies (LDS DMA) from a scalar base address plus a per-lane
 // 32-bit offset (the scalar-base form streams several times faster than one
@@ -155,10 +153,24 @@ __device__ __forceinline__ void wait_stage(int later) {
   }
 }
 
-__device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
-  const u32x4 x0 = *reinterpret_cast<const u32x4*>(tile + swz(row, g));
-  const u32x4 x1 = *reinterpret_cast<const u32x4*>(tile + swz(row, 2 + g));
+// LDS reads at integer LDS byte addresses, so that a per-lane base plus a
+// per-step offset is formed once and each fragment's offset within the stage
+// becomes the instruction's immediate offset.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+__device__ __forceinline__ v8i lds_frag(uint32_t a0, uint32_t a1) {
+  const u32x4 x0 = *(lds_u32x4*)a0;
+  const u32x4 x1 = *(lds_u32x4*)a1;
   return __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ int lds_byte(uint32_t a) { return (int)*(lds_u8*)a; }
+
+// A value the compiler must take as computed here: stops it from
+// re-associating a per-step base with per-fragment constants and hoisting
+// the sums out of the loop, one register each.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Expert table kept in LDS for the whole launch: exclusive prefix of tiles
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ ExpertTable table;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t esz = OUT_BF16 ? 2 : 4;
 
@@ -363,22 +375,34 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     dma4(sb_base + 16 * grp, (uint32_t)(r * (int)p.ldsb + col),
          buf + kScOffB + (wave * 64 + j * 16) * kScaleRow);
   };
-  // part q (0..7) of the data copies of stage kt: rows 64 w + 16 (q/2) .. + 16
-  // of A (q even) or B (q odd)
-  auto data_part = [&](int kt, int q) {
-    const int64_t kb = (int64_t)kt * BK;
-    const uint32_t base = lds_ring + (uint32_t)((kt % kStages) * kStageBytes);
+  // Copies of one stage: scalar source bases and LDS destination, formed
+  // once per stage; part q (0..7) copies rows 64 w + 16 (q/2) .. + 16 of A
+  // (q even) or B (q odd).
+  struct StageCopy {
+    const uint8_t* ak;
+    const uint8_t* bk;
+    uint32_t lds;
+  };
+  auto stage_copy = [&](int kt) {
+    StageCopy c;
+    c.ak = a_base + (int64_t)kt * BK;
+    c.bk = b_base + (int64_t)kt * BK;
+    c.lds = lds_ring + (uint32_t)((kt % kStages) * kStageBytes) + (uint32_t)(wave * 64 * BK);
+    return c;
+  };
+  auto data_part = [&](const StageCopy& c, int q) {
     const int j = q >> 1;
     if ((q & 1) == 0)
-      dma16(a_base + kb, va[j], base + (wave * 64 + j * 16) * BK);
+      dma16(c.ak, va[j], c.lds + j * 16 * BK);
     else
-      dma16(b_base + kb, vb[j], base + kOffB + (wave * 64 + j * 16) * BK);
+      dma16(c.bk, vb[j], c.lds + kOffB + j * 16 * BK);
   };
   // a whole stage at once (first stages of a tile)
   auto issue = [&](int kt) {
     __builtin_amdgcn_sched_barrier(0);
+    const StageCopy c = stage_copy(kt);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) data_part(kt, q);
+    for (int q = 0; q < 8; ++q) data_part(c, q);
     if (kt % kScaleSteps == 0)
 #pragma unroll
       for (int j = 0; j < 4; ++j) scale_part(kt / kScaleSteps, j);
@@ -390,22 +414,42 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   // other set is filled from stage kt + 1
   v8i af[2][4], bf[2][4];
   int as[2][4], bs[2][4];
-  // the scale byte of (row, stage kt) for this lane's block half
-  auto scale_at = [&](int kt, int off_row) {
-    const uint8_t* sc = smem + kStages * kStageBytes + ((kt / kScaleSteps) & 1) * kScaleBuf;
-    return (int)sc[off_row * kScaleRow + 2 * (kt % kScaleSteps) + fg];
+  // Per-lane LDS offsets of this wave's fragments inside a stage: row
+  // wm WT + fr (A) or wn WT + fr (B), chunks g and 2 + g under the swizzle,
+  // which for rows 32 i + fr depends on fr only; fragment i adds 32 rows =
+  // 2048 bytes.  Scale bytes: row * 16 + 2 (kt % 8) + g.
+  const int swzc = (fr >> 1) & 3;
+  const uint32_t rA = (uint32_t)((wm * WT + fr) * BK + ((fg ^ swzc) << 4));
+  const uint32_t rB = (uint32_t)(kOffB + (wn * WT + fr) * BK + ((fg ^ swzc) << 4));
+  const uint32_t rX = (uint32_t)((((2 + fg) ^ swzc) - (fg ^ swzc)) << 4);   // +-32: chunk 2 + g
+  const uint32_t rSA = (uint32_t)((wm * WT + fr) * kScaleRow + fg);
+  const uint32_t rSB = (uint32_t)(kScOffB + (wn * WT + fr) * kScaleRow + fg);
+  // this lane's LDS addresses of fragment 0 of stage kt (A chunk g, A chunk
+  // 2 + g, B chunk g, B chunk 2 + g, A scale, B scale); fragment i adds an
+  // immediate offset
+  struct StageRead {
+    uint32_t a0, a1, b0, b1, sa, sb;
   };
-  auto load_b = [&](int kt, int set, int j) {
-    const uint8_t* base = smem + (kt % kStages) * kStageBytes;
-    const int r = wn * WT + j * 32 + fr;
-    bf[set][j] = frag(base + kOffB, r, fg);
-    bs[set][j] = scale_at(kt, BM + r);
+  auto stage_read = [&](int kt) {
+    const uint32_t data = lds_ring + (uint32_t)((kt % kStages) * kStageBytes);
+    const uint32_t scale = lds_sc + (uint32_t)(((kt / kScaleSteps) & 1) * kScaleBuf) +
+                           (uint32_t)(2 * (kt % kScaleSteps));
+    StageRead r;
+    r.a0 = opaque(data + rA);
+    r.a1 = opaque(r.a0 + rX);
+    r.b0 = opaque(data + rB);
+    r.b1 = opaque(r.b0 + rX);
+    r.sa = opaque(scale + rSA);
+    r.sb = opaque(scale + rSB);
+    return r;
   };
-  auto load_a = [&](int kt, int set, int i) {
-    const uint8_t* base = smem + (kt % kStages) * kStageBytes;
-    const int r = wm * WT + i * 32 + fr;
-    af[set][i] = frag(base, r, fg);
-    as[set][i] = scale_at(kt, r);
+  auto load_a = [&](const StageRead& r, int set, int i) {
+    af[set][i] = lds_frag(r.a0 + i * 32 * BK, r.a1 + i * 32 * BK);
+    as[set][i] = lds_byte(r.sa + i * 32 * kScaleRow);
+  };
+  auto load_b = [&](const StageRead& r, int set, int j) {
+    bf[set][j] = lds_frag(r.b0 + j * 32 * BK, r.b1 + j * 32 * BK);
+    bs[set][j] = lds_byte(r.sb + j * 32 * kScaleRow);
   };
 
   int tile = blockIdx.x;
@@ -429,10 +473,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       // or store of this wave, and at most 3 later stages follow them
       wait_stage(min(nk - 1, 3));
       __syncthreads();
+      const StageRead r0 = stage_read(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        load_a(0, 0, i);
-        load_b(0, 0, i);
+        load_a(r0, 0, i);
+        load_b(r0, 0, i);
       }
     }
 
@@ -456,42 +501,54 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // longer between two MFMAs idles the matrix pipe): the reads of stage
     // kt+1 into the other set, the 8 copies of stage kt+4 into the freed
     // buffer, and the scale group that starts at stage kt+4.
-#define MX_STEP(KT, SET)                                                                    \
+#define MX_STEP(KT, SET, FULL)                                                              \
   {                                                                                         \
     const int kt_ = (KT);                                                                   \
-    const bool nx_ = kt_ + 1 < nk;                                                          \
-    const bool pf_ = kt_ + 4 < nk;                                                          \
+    const bool nx_ = (FULL) || kt_ + 1 < nk;                                                \
+    const bool pf_ = (FULL) || kt_ + 4 < nk;                                                \
     const bool sg_ = pf_ && ((kt_ + 4) % kScaleSteps == 0);                                 \
     const int g_ = (kt_ + 4) / kScaleSteps;                                                 \
     __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage kt */    \
     if (nx_) {                                                                              \
-      wait_stage(min(nk - 2 - kt_, kStages - 2));                                           \
+      if (FULL)                                                                             \
+        wait_stage(kStages - 2);                                                            \
+      else                                                                                  \
+        wait_stage(min(nk - 2 - kt_, kStages - 2));                                         \
       __syncthreads();                                                                      \
     }                                                                                       \
+    const StageRead rd_ = stage_read(kt_ + 1);                                              \
+    const StageCopy cp_ = stage_copy(kt_ + 4);                                              \
     MX_FENCE                                                                                \
-    MX_MFMA(0, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 0); MX_FENCE                     \
-    MX_MFMA(0, 1, SET) if (pf_) data_part(kt_ + 4, 0); MX_FENCE                             \
-    MX_MFMA(0, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 0); MX_FENCE                     \
-    MX_MFMA(0, 3, SET) if (pf_) data_part(kt_ + 4, 1); MX_FENCE                             \
-    MX_MFMA(1, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 1); MX_FENCE                     \
-    MX_MFMA(1, 1, SET) if (pf_) data_part(kt_ + 4, 2); MX_FENCE                             \
-    MX_MFMA(1, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 1); MX_FENCE                     \
-    MX_MFMA(1, 3, SET) if (pf_) data_part(kt_ + 4, 3); MX_FENCE                             \
-    MX_MFMA(2, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 2); MX_FENCE                     \
-    MX_MFMA(2, 1, SET) if (pf_) data_part(kt_ + 4, 4); MX_FENCE                             \
-    MX_MFMA(2, 2, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 2); MX_FENCE                     \
-    MX_MFMA(2, 3, SET) if (pf_) data_part(kt_ + 4, 5); MX_FENCE                             \
-    MX_MFMA(3, 0, SET) if (nx_) load_a(kt_ + 1, (SET) ^ 1, 3); if (pf_) data_part(kt_ + 4, 6); \
+    MX_MFMA(0, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 0); MX_FENCE                         \
+    MX_MFMA(0, 1, SET) if (pf_) data_part(cp_, 0); MX_FENCE                                 \
+    MX_MFMA(0, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 0); MX_FENCE                         \
+    MX_MFMA(0, 3, SET) if (pf_) data_part(cp_, 1); MX_FENCE                                 \
+    MX_MFMA(1, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 1); MX_FENCE                         \
+    MX_MFMA(1, 1, SET) if (pf_) data_part(cp_, 2); MX_FENCE                                 \
+    MX_MFMA(1, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 1); MX_FENCE                         \
+    MX_MFMA(1, 3, SET) if (pf_) data_part(cp_, 3); MX_FENCE                                 \
+    MX_MFMA(2, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 2); MX_FENCE                         \
+    MX_MFMA(2, 1, SET) if (pf_) data_part(cp_, 4); MX_FENCE                                 \
+    MX_MFMA(2, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 2); MX_FENCE                         \
+    MX_MFMA(2, 3, SET) if (pf_) data_part(cp_, 5); MX_FENCE                                 \
+    MX_MFMA(3, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 3); if (pf_) data_part(cp_, 6);      \
     MX_FENCE                                                                                \
-    MX_MFMA(3, 1, SET) if (nx_) load_b(kt_ + 1, (SET) ^ 1, 3); if (pf_) data_part(kt_ + 4, 7); \
+    MX_MFMA(3, 1, SET) if (nx_) load_b(rd_, (SET) ^ 1, 3); if (pf_) data_part(cp_, 7);      \
     MX_FENCE                                                                                \
     MX_MFMA(3, 2, SET) if (sg_) { scale_part(g_, 0); scale_part(g_, 1); } MX_FENCE          \
     MX_MFMA(3, 3, SET) if (sg_) { scale_part(g_, 2); scale_part(g_, 3); } MX_FENCE          \
   }
 
-    for (int kt = 0; kt < nk; kt += 2) {
-      MX_STEP(kt, 0)
-      MX_STEP(kt + 1, 1)
+    // steady state (every step reads its successor and copies stage kt+4),
+    // then the last 2 or 4 steps of the tile with those checks
+    int kt = 0;
+    for (; kt + 5 < nk; kt += 2) {
+      MX_STEP(kt, 0, true)
+      MX_STEP(kt + 1, 1, true)
+    }
+    for (; kt < nk; kt += 2) {
+      MX_STEP(kt, 0, false)
+      MX_STEP(kt + 1, 1, false)
     }
 #undef MX_STEP
 #undef MX_FENCE

@@ -18,12 +18,20 @@ value = 3 * 2 T N K / step time (TFLOP/s over the whole step, quantize
 kernels included).  The grouped-GEMM roofline uses the GEMM launches' own
 durations, measured with events on the stream they run on.
 
+HBM traffic of the GEMM launches (roofline "traffic") comes from the FETCH_SIZE
+and WRITE_SIZE counter summary under profiles/, scaled by the same counters
+read on a plain device copy of known size (--calibrate-copy); it is reported
+only while the GEMM source still hashes to the one the counters were taken on.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --calibrate-copy      (copy of 1 GiB, for counter scaling)
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,6 +41,9 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "moe8_h4096_f14336"
 PEAK_MXFP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+GEMM_SOURCES = ["moe_expert_grouped_group_amd/csrc/gemm.hip",
+                "moe_expert_grouped_group_amd/csrc/mx_device.h"]
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -42,7 +53,48 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB three times (counter scaling)")
     return ap.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
+    """HBM bytes per GEMM launch from the counter summary, or None when the
+    summary is missing or was taken on a different GEMM source."""
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "copies": 4,
+                      "read_bytes_per_copy": COPY_BYTES, "write_bytes_per_copy": COPY_BYTES}),
+          flush=True)
 
 
 def cpu_baseline(w, budget_rows=1024, n_cols=2048):
@@ -89,6 +141,9 @@ def cpu_baseline(w, budget_rows=1024, n_cols=2048):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MXFP8 grouped-GEMM "
               "path here has no multi-GPU mode.", file=sys.stderr)
@@ -204,7 +259,8 @@ def main():
         "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": stored_traffic(args.workload),
                      "kernel": "grouped_gemm_kernel (3 launches per step)"},
         "quantize_roofline": {"bound": "hbm", "achieved": round(quant_gbs, 1),
                               "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -54,8 +54,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256;        // output rows per workgroup tile
 constexpr int BN = 256;        // output columns per workgroup tile
-constexpr int BK = 64;         // contraction bytes per stage (one MFMA step)
-constexpr int kStages = 4;     // LDS ring depth
+constexpr int BK = 128;        // contraction bytes per LDS stage: one 128-byte line per row
+constexpr int KSTEP = 64;      // contraction bytes per MFMA step (two steps per stage)
+constexpr int kSlots = 2;      // LDS stages
 constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 128 x 128
 constexpr int WT = 128;        // wave tile edge
 constexpr int kMaxGroups = 1024;
@@ -79,26 +80,26 @@ struct GemmArgs {
   int32_t ntiles;                      // K-grouped: G * band * ntiles_n tiles
 };
 
-// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK], 16-byte chunk c
-// of row r stored at chunk position c ^ ((r >> 1) & 3).  The LDS has 32
-// banks of 4 bytes, so two 64-byte rows share one bank line; the 8
-// consecutive rows of a fragment read that the LDS serves together then use
-// 8 distinct 16-byte bank groups.
+// LDS layout of one stage: A tile [BM][BK], B tile [BN][BK]; 16-byte chunk c
+// of row r is stored at chunk position c ^ (r & 7).  The LDS has 32 banks of
+// 4 bytes, so each 128-byte row is one bank line and the 8 consecutive rows of
+// a fragment read that the LDS serves together use 8 distinct 16-byte bank
+// groups.  Each row of a stage is one whole cache line of the operand: copies
+// of half lines (64 contraction bytes per row and stage) fetch every line from
+// memory twice and stall the copy path on the outstanding misses.
 constexpr int kTileBytesA = BM * BK;
 constexpr int kTileBytesB = BN * BK;
 constexpr int kOffB = kTileBytesA;
 constexpr int kStageBytes = kTileBytesA + kTileBytesB;
-constexpr int kDmaPerStage = 8;    // per wave: 4 (A) + 4 (B) data copies
-// E8M0 scales arrive in groups of kScaleSteps stages: 16 bytes (16 blocks of
-// 32) per operand row, [BM][16] for A then [BN][16] for B, double-buffered.
-// Copying a row's scale bytes one stage at a time would cost one cache-line
-// request per row per stage for 2 bytes of data, as many requests as the
-// operand tiles themselves.
+constexpr int kDmaHalf = 8;        // per wave and stage: 8 copies of A rows, then 8 of B rows
+// E8M0 scales arrive in groups of kScaleSteps MFMA steps: 16 bytes (16 blocks
+// of 32) per operand row, [BM][16] for A then [BN][16] for B, double-buffered.
+// Copying a row's scale bytes one step at a time would cost one cache-line
+// request per row per step for 2 bytes of data.
 constexpr int kScaleSteps = 8;
 constexpr int kScaleRow = 2 * kScaleSteps;   // bytes per row and group
 constexpr int kScOffB = BM * kScaleRow;
 constexpr int kScaleBuf = (BM + BN) * kScaleRow;
-constexpr int kScaleDma = 8;       // per wave and group: 4 (A) + 4 (B), 16 rows each
 
 // Global -> LDS copies (LDS DMA) from a scalar base address plus a per-lane
 // 32-bit offset (the scalar-base form streams several times faster than one
@@ -136,23 +137,6 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q) {
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// Wait until this wave's copies of the needed stage have landed, given that
-// `later` stages were issued after it (at most kStages - 1 = 3).  A
-// stage that opens a scale group carries kScaleDma more copies; counting only
-// the kDmaPerStage data copies of the later stages waits for at least as many
-// completions as needed (copies complete in issue order).
-__device__ __forceinline__ void wait_stage(int later) {
-  if (later >= 3) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kDmaPerStage));
-  } else if (later == 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaPerStage));
-  } else if (later == 1) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerStage));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
-}
-
 // LDS reads at integer LDS byte addresses, so that a per-lane base plus a
 // per-step offset is formed once and each fragment's offset within the stage
 // becomes the instruction's immediate offset.
@@ -171,6 +155,12 @@ __device__ __forceinline__ int lds_byte(uint32_t a) { return (int)*(lds_u8*)a; }
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+// The same for a scalar pointer stepped through a stage's copies: without it
+// the compiler precomputes every step's address, one register pair each.
+__device__ __forceinline__ const uint8_t* opaque_ptr(const uint8_t* q) {
+  asm volatile("" : "+s"(q));
+  return q;
 }
 
 // Expert table kept in LDS for the whole launch: exclusive prefix of tiles
@@ -249,13 +239,15 @@ __device__ void build_table(const int64_t* __restrict__ m_splits, int G, ExpertT
 
 // One tile's operands.
 struct TileDesc {
-  const uint8_t* a;    // A rows of the tile at contraction 0
+  const uint8_t* a;    // first copied A row of the tile at contraction 0
   const uint8_t* sa;
   const uint8_t* b;
   const uint8_t* sb;
-  char* c;             // C[m0][n0]
-  int32_t nk;          // contraction steps (BK bytes each)
-  int32_t valid_rows;  // rows of A / C that belong to the tile
+  char* c;             // C at the first copied row, first column of the tile
+  int32_t nk;          // MFMA steps (KSTEP contraction bytes each; always even)
+  int32_t row_lo;      // tile rows [row_lo, row_hi) of the copied 256 belong to the tile
+  int32_t row_hi;
+  int32_t rows_avail;  // copied rows inside the operand (256, or T when T < 256)
   int32_t nblk;        // scale blocks of the tile's contraction (nk * 2)
 };
 
@@ -275,14 +267,21 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     const int64_t m0 = t->roff[g] + (int64_t)(mt - t->tpre[g]) * BM;
     const int64_t n0 = (int64_t)nt * BN;
     const int64_t end = min(t->roff[g + 1], p.rows);   // never past the token count
-    d.valid_rows = (int32_t)max(min((int64_t)BM, end - m0), (int64_t)0);
-    d.a = p.a + m0 * p.lda;
-    d.sa = p.sa + m0 * p.ldsa;
+    const int64_t valid = max(min((int64_t)BM, end - m0), (int64_t)0);
+    // The 256 copied rows start at m0c: moved back from the tile's first row
+    // m0 where the tile would run past the last token, so that every copy
+    // stays inside the operand (T < 256 leaves T rows to copy).
+    const int64_t m0c = min(m0, max(p.rows - BM, (int64_t)0));
+    d.rows_avail = (int32_t)min((int64_t)BM, p.rows - m0c);
+    d.row_lo = (int32_t)(m0 - m0c);
+    d.row_hi = d.row_lo + (int32_t)valid;
+    d.a = p.a + m0c * p.lda;
+    d.sa = p.sa + m0c * p.ldsa;
     d.b = p.b + g * p.b_gstride + n0 * p.ldb;
     d.sb = p.sb + g * p.sb_gstride + n0 * p.ldsb;
-    d.nk = d.valid_rows > 0 ? (int32_t)(p.kc / BK) : 0;
+    d.nk = valid > 0 ? (int32_t)(p.kc / KSTEP) : 0;
     d.nblk = (int32_t)(p.kc / 32);
-    d.c = reinterpret_cast<char*>(p.c) + (m0 * p.ldc + n0) * esz;
+    d.c = reinterpret_cast<char*>(p.c) + (m0c * p.ldc + n0) * esz;
   } else {
     const int per_expert = p.band * p.ntiles_n;
     const int g = t->order[tile / per_expert];
@@ -293,12 +292,14 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     const int64_t off = min(t->roff[g], p.kc) & ~(int64_t)127;
     const int64_t len = max(min(t->roff[g + 1], p.kc) - off, (int64_t)0) & ~(int64_t)127;
     const int64_t m0 = (int64_t)mtl * BM, n0 = (int64_t)nt * BN;
-    d.valid_rows = BM;
+    d.row_lo = 0;
+    d.row_hi = BM;
+    d.rows_avail = BM;
     d.a = p.a + m0 * p.lda + off;
     d.sa = p.sa + m0 * p.ldsa + off / 32;
     d.b = p.b + n0 * p.ldb + off;
     d.sb = p.sb + n0 * p.ldsb + off / 32;
-    d.nk = (int32_t)(len / BK);
+    d.nk = (int32_t)(len / KSTEP);
     d.nblk = (int32_t)(len / 32);
     d.c = reinterpret_cast<char*>(p.c) + (g * p.c_gstride + m0 * p.ldc + n0) * esz;
   }
@@ -310,13 +311,15 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
   d.c = (char*)uniform_ptr((const uint8_t*)d.c);
   d.nk = __builtin_amdgcn_readfirstlane(d.nk);
   d.nblk = __builtin_amdgcn_readfirstlane(d.nblk);
-  d.valid_rows = __builtin_amdgcn_readfirstlane(d.valid_rows);
+  d.row_lo = __builtin_amdgcn_readfirstlane(d.row_lo);
+  d.row_hi = __builtin_amdgcn_readfirstlane(d.row_hi);
+  d.rows_avail = __builtin_amdgcn_readfirstlane(d.rows_avail);
   return d;
 }
 
 template <bool KGROUPED, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + 2 * kScaleBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,113 +331,109 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   build_table<KGROUPED>(p.m_splits, p.G, &table, reinterpret_cast<int64_t*>(smem));
   const int ntiles = __builtin_amdgcn_readfirstlane(KGROUPED ? p.ntiles : table.tpre[p.G] * p.ntiles_n);
 
-  // per-lane DMA geometry: wave w copies rows [64 w, 64 w + 64) of the A and
-  // B tiles, 16 rows (1 KB) per instruction: lane i -> row 16 j + i/4, LDS
-  // chunk slot i%4, which holds global chunk (i%4) ^ ((row >> 1) & 3).  The
-  // scale groups use the same rows, 16 rows x 16 bytes per instruction: lane
-  // i -> row 16 j + i/4, bytes 4 (i%4) .. 4 (i%4) + 3 of the row's group.
+  // Copy geometry: wave w copies rows [64 w, 64 w + 64) of the A and the B
+  // tile, 8 rows x 128 bytes per instruction: lane i -> row 8 j + i/8, LDS
+  // chunk position i%8, which holds the row's chunk (i%8) ^ (i/8).  The scale
+  // groups use 16 rows x 16 bytes per instruction: lane i -> row 16 j + i/4,
+  // bytes 4 (i%4) .. 4 (i%4) + 3 of the row's group.
+  const int cr = lane >> 3;
+  const int cchunk = (lane & 7) ^ cr;
   const int dr = lane >> 2;
-  const int dchunk = (lane & 3) ^ ((dr >> 1) & 3);
   const int scol = (lane & 3) * 4;
   const int fr = lane & 31;   // operand row within a 32-row fragment
   const int fg = lane >> 5;   // contraction half of the lane
 
-  uint32_t va[4], vb[4];
+  // Per-lane copy offsets (launch constants): row i/8 of an 8-row part and
+  // its swizzled chunk; rows of the part and of the wave go into the scalar
+  // base.  A wave whose 64 rows would lie past the operand (T < 256) copies
+  // rows of the first waves instead; their results are not stored.
+  const uint32_t ca = (uint32_t)(cr * p.lda + cchunk * 16);
+  const uint32_t cb = (uint32_t)(cr * p.ldb + cchunk * 16);
+  const uint32_t csa = (uint32_t)(dr * p.ldsa);
+  const uint32_t csb = (uint32_t)(dr * p.ldsb);
   const uint8_t *a_base, *b_base, *sa_base, *sb_base;
-  int s_valid, s_nblk;
+  int s_nblk;
   auto setup = [&](const TileDesc& d) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave * 64 + j * 16 + dr;
-      const int ra = r < d.valid_rows ? r : 0;   // rows past the expert: any valid row
-      va[j] = (uint32_t)(ra * p.lda + dchunk * 16);
-      vb[j] = (uint32_t)(r * p.ldb + dchunk * 16);
-    }
-    a_base = uniform_ptr(d.a);
-    b_base = uniform_ptr(d.b);
-    sa_base = uniform_ptr(d.sa);
-    sb_base = uniform_ptr(d.sb);
-    s_valid = d.valid_rows;
+    const int64_t wrow = (int64_t)((wave * 64) % d.rows_avail);
+    a_base = uniform_ptr(d.a + wrow * p.lda);
+    sa_base = uniform_ptr(d.sa + wrow * p.ldsa);
+    b_base = uniform_ptr(d.b + (int64_t)wave * 64 * p.ldb);
+    sb_base = uniform_ptr(d.sb + (int64_t)wave * 64 * p.ldsb);
     s_nblk = d.nblk;
   };
-  // LDS byte addresses of the stage ring and of the scale buffers (the low
-  // half of the generic address of an LDS object is its LDS address)
+  // LDS byte addresses of the stages and of the scale buffers (the low half
+  // of the generic address of an LDS object is its LDS address)
   const uint32_t lds_ring = (uint32_t)(uintptr_t)smem;
-  const uint32_t lds_sc = lds_ring + kStages * kStageBytes;
-  // Scale group `grp` (blocks [16 grp, 16 grp + 16) of every row) into buffer
-  // grp % 2.  In a K-grouped tile the last group may run past the expert's
-  // blocks (s_nblk, a multiple of 4): those lanes re-read the last valid word.
-  // part j (0..3) of scale group grp: rows 64 w + 16 j .. + 16 of A and of B
+  const uint32_t lds_sc = lds_ring + kSlots * kStageBytes;
+  // Part j (0..3) of scale group grp (blocks [16 grp, 16 grp + 16) of every
+  // row, MFMA steps [8 grp, 8 grp + 8)) into buffer grp % 2: rows 64 w + 16 j
+  // .. + 16 of A and of B.  In a K-grouped tile the last group may run past
+  // the expert's blocks (s_nblk, a multiple of 4): those lanes re-read the
+  // last valid word.
   auto scale_part = [&](int grp, int j) {
     const uint32_t buf = lds_sc + (uint32_t)((grp & 1) * kScaleBuf);
-    const int col = KGROUPED ? max(min(scol, s_nblk - 4 - 16 * grp), 0) : scol;
-    const int r = wave * 64 + j * 16 + dr;
-    const int ra = r < s_valid ? r : 0;
-    dma4(sa_base + 16 * grp, (uint32_t)(ra * (int)p.ldsa + col),
+    const uint32_t col = (uint32_t)(KGROUPED ? max(min(scol, s_nblk - 4 - 16 * grp), 0) : scol);
+    dma4(sa_base + (int64_t)j * 16 * p.ldsa + 16 * grp, csa + col,
          buf + (wave * 64 + j * 16) * kScaleRow);
-    dma4(sb_base + 16 * grp, (uint32_t)(r * (int)p.ldsb + col),
+    dma4(sb_base + (int64_t)j * 16 * p.ldsb + 16 * grp, csb + col,
          buf + kScOffB + (wave * 64 + j * 16) * kScaleRow);
   };
-  // Copies of one stage: scalar source bases and LDS destination, formed
-  // once per stage; part q (0..7) copies rows 64 w + 16 (q/2) .. + 16 of A
-  // (q even) or B (q odd).
+  // Copies of stage st (contraction bytes [128 st, 128 st + 128)) into LDS
+  // slot st % 2, part by part (rows 64 w + 8 j .. + 8, j = 0..7): a scalar
+  // source pointer and LDS destination per operand, each advanced by one
+  // part after its copy.
   struct StageCopy {
     const uint8_t* ak;
     const uint8_t* bk;
-    uint32_t lds;
+    uint32_t la, lb;
   };
-  auto stage_copy = [&](int kt) {
+  const int64_t a_part = 8 * p.lda, b_part = 8 * p.ldb;
+  auto stage_copy = [&](int st) {
     StageCopy c;
-    c.ak = a_base + (int64_t)kt * BK;
-    c.bk = b_base + (int64_t)kt * BK;
-    c.lds = lds_ring + (uint32_t)((kt % kStages) * kStageBytes) + (uint32_t)(wave * 64 * BK);
+    c.ak = a_base + (int64_t)st * BK;
+    c.bk = b_base + (int64_t)st * BK;
+    c.la = lds_ring + (uint32_t)((st % kSlots) * kStageBytes) + (uint32_t)(wave * 64 * BK);
+    c.lb = c.la + kOffB;
     return c;
   };
-  auto data_part = [&](const StageCopy& c, int q) {
-    const int j = q >> 1;
-    if ((q & 1) == 0)
-      dma16(c.ak, va[j], c.lds + j * 16 * BK);
-    else
-      dma16(c.bk, vb[j], c.lds + kOffB + j * 16 * BK);
+  auto copy_a = [&](StageCopy& c) {
+    dma16(c.ak, ca, c.la);
+    c.ak = opaque_ptr(c.ak + a_part);
+    c.la += 8 * BK;
   };
-  // a whole stage at once (first stages of a tile)
-  auto issue = [&](int kt) {
-    __builtin_amdgcn_sched_barrier(0);
-    const StageCopy c = stage_copy(kt);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) data_part(c, q);
-    if (kt % kScaleSteps == 0)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) scale_part(kt / kScaleSteps, j);
-    __builtin_amdgcn_sched_barrier(0);
+  auto copy_b = [&](StageCopy& c) {
+    dma16(c.bk, cb, c.lb);
+    c.bk = opaque_ptr(c.bk + b_part);
+    c.lb += 8 * BK;
   };
 
   v16f acc[4][4];
-  // fragments of two stages: set kt & 1 feeds the MFMAs of step kt while the
-  // other set is filled from stage kt + 1
+  // fragments of two MFMA steps: set kt & 1 feeds the MFMAs of step kt while
+  // the other set is filled for step kt + 1
   v8i af[2][4], bf[2][4];
   int as[2][4], bs[2][4];
-  // Per-lane LDS offsets of this wave's fragments inside a stage: row
-  // wm WT + fr (A) or wn WT + fr (B), chunks g and 2 + g under the swizzle,
-  // which for rows 32 i + fr depends on fr only; fragment i adds 32 rows =
-  // 2048 bytes.  Scale bytes: row * 16 + 2 (kt % 8) + g.
-  const int swzc = (fr >> 1) & 3;
-  const uint32_t rA = (uint32_t)((wm * WT + fr) * BK + ((fg ^ swzc) << 4));
-  const uint32_t rB = (uint32_t)(kOffB + (wn * WT + fr) * BK + ((fg ^ swzc) << 4));
-  const uint32_t rX = (uint32_t)((((2 + fg) ^ swzc) - (fg ^ swzc)) << 4);   // +-32: chunk 2 + g
+  // Per-lane LDS offsets of this wave's fragments: row wm WT + fr (A) or
+  // wn WT + fr (B); for step half h the lane's chunks are 4 h + g and
+  // 4 h + 2 + g, at positions p0 ^ 4h and p0 ^ 4h ^ 2 with p0 = g ^ (fr & 7)
+  // (fragment rows 32 i + fr share fr & 7); fragment i adds 32 rows.
+  const int p0 = fg ^ (fr & 7);
+  const uint32_t rA = (uint32_t)((wm * WT + fr) * BK + p0 * 16);
+  const uint32_t rB = (uint32_t)(kOffB + (wn * WT + fr) * BK + p0 * 16);
+  const uint32_t rX = (uint32_t)(((p0 ^ 2) - p0) * 16);   // +-32: chunk 2 + g
+  const uint32_t rH = (uint32_t)(((p0 ^ 4) - p0) * 16);   // +-64: second half of the stage
   const uint32_t rSA = (uint32_t)((wm * WT + fr) * kScaleRow + fg);
   const uint32_t rSB = (uint32_t)(kScOffB + (wn * WT + fr) * kScaleRow + fg);
-  // this lane's LDS addresses of fragment 0 of stage kt (A chunk g, A chunk
-  // 2 + g, B chunk g, B chunk 2 + g, A scale, B scale); fragment i adds an
-  // immediate offset
-  struct StageRead {
+  // this lane's LDS addresses of fragment 0 of MFMA step kt (A chunk g, A
+  // chunk 2 + g, B chunk g, B chunk 2 + g, A scale, B scale)
+  struct StepRead {
     uint32_t a0, a1, b0, b1, sa, sb;
   };
-  auto stage_read = [&](int kt) {
-    const uint32_t data = lds_ring + (uint32_t)((kt % kStages) * kStageBytes);
+  auto step_read = [&](int kt) {
+    const uint32_t data = lds_ring + (uint32_t)(((kt >> 1) % kSlots) * kStageBytes) +
+                          ((kt & 1) ? rH : 0u);
     const uint32_t scale = lds_sc + (uint32_t)(((kt / kScaleSteps) & 1) * kScaleBuf) +
                            (uint32_t)(2 * (kt % kScaleSteps));
-    StageRead r;
+    StepRead r;
     r.a0 = opaque(data + rA);
     r.a1 = opaque(r.a0 + rX);
     r.b0 = opaque(data + rB);
@@ -443,24 +442,45 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     r.sb = opaque(scale + rSB);
     return r;
   };
-  auto load_a = [&](const StageRead& r, int set, int i) {
+  auto load_a = [&](const StepRead& r, int set, int i) {
     af[set][i] = lds_frag(r.a0 + i * 32 * BK, r.a1 + i * 32 * BK);
     as[set][i] = lds_byte(r.sa + i * 32 * kScaleRow);
   };
-  auto load_b = [&](const StageRead& r, int set, int j) {
+  auto load_b = [&](const StepRead& r, int set, int j) {
     bf[set][j] = lds_frag(r.b0 + j * 32 * BK, r.b1 + j * 32 * BK);
     bs[set][j] = lds_byte(r.sb + j * 32 * kScaleRow);
+  };
+  // First copies of a tile: stage 0 (A and B rows, scale group 0) and the A
+  // rows of stage 1; the B rows of stage 1 follow in step 0.
+  auto tile_prologue = [&](int nk) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk > 0) {
+      StageCopy c0 = stage_copy(0);
+#pragma unroll
+      for (int j = 0; j < kDmaHalf; ++j) {
+        copy_a(c0);
+        copy_b(c0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) scale_part(0, j);
+    }
+    if (nk > 2) {
+      StageCopy c1 = stage_copy(1);
+#pragma unroll
+      for (int j = 0; j < kDmaHalf; ++j) copy_a(c1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   int tile = blockIdx.x;
   if (tile >= ntiles) return;
   TileDesc cur = describe<KGROUPED>(p, &table, tile, esz);
   setup(cur);
-  for (int s = 0; s < kStages; ++s)
-    if (s < cur.nk) issue(s);
+  tile_prologue(cur.nk);
 
   for (;;) {
     const int nk = cur.nk;
+    const int ns = nk >> 1;   // stages
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -469,11 +489,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     if (nk > 0) {
-      // stage 0 of this tile: its copies were issued before any later copy
-      // or store of this wave, and at most 3 later stages follow them
-      wait_stage(min(nk - 1, 3));
+      // stage 0: only the A rows of stage 1 (if any) were issued after it
+      // (copies complete in issue order; stores of the previous tile can only
+      // make this wait longer)
+      if (ns > 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaHalf));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      const StageRead r0 = stage_read(0);
+      const StepRead r0 = step_read(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         load_a(r0, 0, i);
@@ -492,71 +516,94 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_sched_barrier(0);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
 
-    // One step (16 MFMAs per wave) on the fragments of stage kt, held in
-    // registers (set SET) since the previous step.  The step opens with the
-    // only barrier: before it this wave waits for its LDS reads of stage kt
-    // and for its copies of stage kt+1; after it stage kt+1 is visible to
-    // every wave and buffer kt % kStages is free.  The MFMAs then run with
-    // one item of other work after each (with one wave per SIMD, anything
-    // longer between two MFMAs idles the matrix pipe): the reads of stage
-    // kt+1 into the other set, the 8 copies of stage kt+4 into the freed
-    // buffer, and the scale group that starts at stage kt+4.
-#define MX_STEP(KT, SET, FULL)                                                              \
+    // Two MFMA steps per stage st, 16 MFMAs per wave each, every MFMA
+    // followed by at most one fragment read and one copy (with one wave per
+    // SIMD, more between two MFMAs idles the matrix pipe).
+    // Even step 2 st: MFMAs on set 0 (step 2 st); reads of step 2 st + 1
+    // (second half of stage st, already resident) into set 1; copies of the
+    // B rows of stage st + 1.
+    // Odd step 2 st + 1: this wave waits for its LDS reads of stage st and
+    // for all its copies (stage st + 1 is the newest complete one), then the
+    // barrier makes stage st + 1 visible and frees slot st % 2; MFMAs on set
+    // 1; reads of step 2 st + 2 (stage st + 1) into set 0; copies of the A
+    // rows of stage st + 2 into the freed slot, and the scale group that
+    // starts there.
+#define MX_EVEN(ST, FULL)                                                                   \
   {                                                                                         \
-    const int kt_ = (KT);                                                                   \
-    const bool nx_ = (FULL) || kt_ + 1 < nk;                                                \
-    const bool pf_ = (FULL) || kt_ + 4 < nk;                                                \
-    const bool sg_ = pf_ && ((kt_ + 4) % kScaleSteps == 0);                                 \
-    const int g_ = (kt_ + 4) / kScaleSteps;                                                 \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage kt */    \
+    const int st_ = (ST);                                                                   \
+    const bool cb_ = (FULL) || st_ + 1 < ns;                                                \
+    const StepRead rd_ = step_read(2 * st_ + 1);                                            \
+    StageCopy cp_ = stage_copy(st_ + 1);                                                    \
+    MX_FENCE                                                                                \
+    MX_MFMA(0, 0, 0) load_a(rd_, 1, 0); MX_FENCE                                            \
+    MX_MFMA(0, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(0, 2, 0) load_b(rd_, 1, 0); MX_FENCE                                            \
+    MX_MFMA(0, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 0, 0) load_a(rd_, 1, 1); MX_FENCE                                            \
+    MX_MFMA(1, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 2, 0) load_b(rd_, 1, 1); MX_FENCE                                            \
+    MX_MFMA(1, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 0, 0) load_a(rd_, 1, 2); MX_FENCE                                            \
+    MX_MFMA(2, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 2, 0) load_b(rd_, 1, 2); MX_FENCE                                            \
+    MX_MFMA(2, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(3, 0, 0) load_a(rd_, 1, 3); MX_FENCE                                            \
+    MX_MFMA(3, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(3, 2, 0) load_b(rd_, 1, 3); MX_FENCE                                            \
+    MX_MFMA(3, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+  }
+#define MX_ODD(ST, FULL)                                                                    \
+  {                                                                                         \
+    const int st_ = (ST);                                                                   \
+    const bool nx_ = (FULL) || st_ + 1 < ns;                                                \
+    const bool pf_ = (FULL) || st_ + 2 < ns;                                                \
+    const bool sg_ = pf_ && (((st_ + 2) * 2) % kScaleSteps == 0);                           \
+    const int g_ = ((st_ + 2) * 2) / kScaleSteps;                                           \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage st */    \
     if (nx_) {                                                                              \
-      if (FULL)                                                                             \
-        wait_stage(kStages - 2);                                                            \
-      else                                                                                  \
-        wait_stage(min(nk - 2 - kt_, kStages - 2));                                         \
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                             \
       __syncthreads();                                                                      \
     }                                                                                       \
-    const StageRead rd_ = stage_read(kt_ + 1);                                              \
-    const StageCopy cp_ = stage_copy(kt_ + 4);                                              \
+    const StepRead rd_ = step_read(2 * st_ + 2);                                            \
+    StageCopy cp_ = stage_copy(st_ + 2);                                                    \
     MX_FENCE                                                                                \
-    MX_MFMA(0, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 0); MX_FENCE                         \
-    MX_MFMA(0, 1, SET) if (pf_) data_part(cp_, 0); MX_FENCE                                 \
-    MX_MFMA(0, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 0); MX_FENCE                         \
-    MX_MFMA(0, 3, SET) if (pf_) data_part(cp_, 1); MX_FENCE                                 \
-    MX_MFMA(1, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 1); MX_FENCE                         \
-    MX_MFMA(1, 1, SET) if (pf_) data_part(cp_, 2); MX_FENCE                                 \
-    MX_MFMA(1, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 1); MX_FENCE                         \
-    MX_MFMA(1, 3, SET) if (pf_) data_part(cp_, 3); MX_FENCE                                 \
-    MX_MFMA(2, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 2); MX_FENCE                         \
-    MX_MFMA(2, 1, SET) if (pf_) data_part(cp_, 4); MX_FENCE                                 \
-    MX_MFMA(2, 2, SET) if (nx_) load_b(rd_, (SET) ^ 1, 2); MX_FENCE                         \
-    MX_MFMA(2, 3, SET) if (pf_) data_part(cp_, 5); MX_FENCE                                 \
-    MX_MFMA(3, 0, SET) if (nx_) load_a(rd_, (SET) ^ 1, 3); if (pf_) data_part(cp_, 6);      \
-    MX_FENCE                                                                                \
-    MX_MFMA(3, 1, SET) if (nx_) load_b(rd_, (SET) ^ 1, 3); if (pf_) data_part(cp_, 7);      \
-    MX_FENCE                                                                                \
-    MX_MFMA(3, 2, SET) if (sg_) { scale_part(g_, 0); scale_part(g_, 1); } MX_FENCE          \
-    MX_MFMA(3, 3, SET) if (sg_) { scale_part(g_, 2); scale_part(g_, 3); } MX_FENCE          \
+    MX_MFMA(0, 0, 1) if (nx_) load_a(rd_, 0, 0); MX_FENCE                                   \
+    MX_MFMA(0, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(0, 2, 1) if (nx_) load_b(rd_, 0, 0); MX_FENCE                                   \
+    MX_MFMA(0, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 0, 1) if (nx_) load_a(rd_, 0, 1); MX_FENCE                                   \
+    MX_MFMA(1, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 2, 1) if (nx_) load_b(rd_, 0, 1); MX_FENCE                                   \
+    MX_MFMA(1, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 0, 1) if (nx_) load_a(rd_, 0, 2); MX_FENCE                                   \
+    MX_MFMA(2, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); MX_FENCE                                   \
+    MX_MFMA(2, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
+    MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (sg_) scale_part(g_, 0); MX_FENCE       \
+    MX_MFMA(3, 1, 1) if (pf_) copy_a(cp_); if (sg_) scale_part(g_, 1); MX_FENCE          \
+    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (sg_) scale_part(g_, 2); MX_FENCE       \
+    MX_MFMA(3, 3, 1) if (pf_) copy_a(cp_); if (sg_) scale_part(g_, 3); MX_FENCE          \
   }
 
-    // steady state (every step reads its successor and copies stage kt+4),
-    // then the last 2 or 4 steps of the tile with those checks
-    int kt = 0;
-    for (; kt + 5 < nk; kt += 2) {
-      MX_STEP(kt, 0, true)
-      MX_STEP(kt + 1, 1, true)
+    // steady state (every stage has a successor two ahead), then the last
+    // two stages with those checks
+    int st = 0;
+    for (; st + 2 < ns; ++st) {
+      MX_EVEN(st, true)
+      MX_ODD(st, true)
     }
-    for (; kt < nk; kt += 2) {
-      MX_STEP(kt, 0, false)
-      MX_STEP(kt + 1, 1, false)
+    for (; st < ns; ++st) {
+      MX_EVEN(st, false)
+      MX_ODD(st, false)
     }
-#undef MX_STEP
+#undef MX_EVEN
+#undef MX_ODD
 #undef MX_FENCE
 #undef MX_MFMA
 
     // Next tile: once every wave has read the last stage (lgkmcnt(0) + the
-    // barrier), all LDS buffers are free, so its first stages are copied
-    // while this tile's results are stored.
+    // barrier), both LDS slots and both scale buffers are free, so its first
+    // stages are copied while this tile's results are stored.
     const int next = tile + gridDim.x;
     TileDesc nxt;
     nxt.nk = 0;
@@ -565,8 +612,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
       setup(nxt);
-      for (int s = 0; s < kStages; ++s)
-        if (s < nxt.nk) issue(s);
+      tile_prologue(nxt.nk);
     }
 
     // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
@@ -580,13 +626,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
       const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (int64_t)(wn * WT + fr) * esz);
-      const int vrows = cur.valid_rows;
+      const int lo = cur.row_lo, hi = cur.row_hi;
+      const bool part = lo > 0 || hi < BM;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
-          if (vrows < BM && row + 4 * fg >= vrows) continue;
+          if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
           char* rbase = cur.c + (int64_t)row * ldc_b + lane_off;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {

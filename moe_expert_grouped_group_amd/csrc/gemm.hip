@@ -450,8 +450,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     bf[set][j] = lds_frag(r.b0 + j * 32 * BK, r.b1 + j * 32 * BK);
     bs[set][j] = lds_byte(r.sb + j * 32 * kScaleRow);
   };
-  // First copies of a tile: stage 0 (A and B rows, scale group 0) and the A
-  // rows of stage 1; the B rows of stage 1 follow in step 0.
+  // First copies of a tile: stages 0 (with scale group 0) and 1.
   auto tile_prologue = [&](int nk) {
     __builtin_amdgcn_sched_barrier(0);
     if (nk > 0) {
@@ -467,7 +466,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     if (nk > 2) {
       StageCopy c1 = stage_copy(1);
 #pragma unroll
-      for (int j = 0; j < kDmaHalf; ++j) copy_a(c1);
+      for (int j = 0; j < kDmaHalf; ++j) {
+        copy_a(c1);
+        copy_b(c1);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -489,11 +491,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     if (nk > 0) {
-      // stage 0: only the A rows of stage 1 (if any) were issued after it
+      // stage 0: only the copies of stage 1 (if any) were issued after it
       // (copies complete in issue order; stores of the previous tile can only
       // make this wait longer)
       if (ns > 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaHalf));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaHalf));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
@@ -517,40 +519,37 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
 
     // Two MFMA steps per stage st, 16 MFMAs per wave each, every MFMA
-    // followed by at most one fragment read and one copy (with one wave per
-    // SIMD, more between two MFMAs idles the matrix pipe).
+    // followed by at most one fragment read and a copy or two (with one wave
+    // per SIMD, more between two MFMAs idles the matrix pipe).
     // Even step 2 st: MFMAs on set 0 (step 2 st); reads of step 2 st + 1
-    // (second half of stage st, already resident) into set 1; copies of the
-    // B rows of stage st + 1.
+    // (second half of stage st, already resident) into set 1.
     // Odd step 2 st + 1: this wave waits for its LDS reads of stage st and
-    // for all its copies (stage st + 1 is the newest complete one), then the
-    // barrier makes stage st + 1 visible and frees slot st % 2; MFMAs on set
-    // 1; reads of step 2 st + 2 (stage st + 1) into set 0; copies of the A
-    // rows of stage st + 2 into the freed slot, and the scale group that
-    // starts there.
+    // for all its copies (stage st + 1 is the newest one), then the barrier
+    // makes stage st + 1 visible and frees slot st % 2; MFMAs on set 1; reads
+    // of step 2 st + 2 (stage st + 1) into set 0; the 16 copies of stage
+    // st + 2 into the freed slot, two steps ahead of their first read, and
+    // the scale group that starts there.
 #define MX_EVEN(ST, FULL)                                                                   \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
-    const bool cb_ = (FULL) || st_ + 1 < ns;                                                \
     const StepRead rd_ = step_read(2 * st_ + 1);                                            \
-    StageCopy cp_ = stage_copy(st_ + 1);                                                    \
     MX_FENCE                                                                                \
     MX_MFMA(0, 0, 0) load_a(rd_, 1, 0); MX_FENCE                                            \
-    MX_MFMA(0, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(0, 1, 0)                                                                        \
     MX_MFMA(0, 2, 0) load_b(rd_, 1, 0); MX_FENCE                                            \
-    MX_MFMA(0, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(0, 3, 0)                                                                        \
     MX_MFMA(1, 0, 0) load_a(rd_, 1, 1); MX_FENCE                                            \
-    MX_MFMA(1, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 1, 0)                                                                        \
     MX_MFMA(1, 2, 0) load_b(rd_, 1, 1); MX_FENCE                                            \
-    MX_MFMA(1, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(1, 3, 0)                                                                        \
     MX_MFMA(2, 0, 0) load_a(rd_, 1, 2); MX_FENCE                                            \
-    MX_MFMA(2, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 1, 0)                                                                        \
     MX_MFMA(2, 2, 0) load_b(rd_, 1, 2); MX_FENCE                                            \
-    MX_MFMA(2, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(2, 3, 0)                                                                        \
     MX_MFMA(3, 0, 0) load_a(rd_, 1, 3); MX_FENCE                                            \
-    MX_MFMA(3, 1, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(3, 1, 0)                                                                        \
     MX_MFMA(3, 2, 0) load_b(rd_, 1, 3); MX_FENCE                                            \
-    MX_MFMA(3, 3, 0) if (cb_) copy_b(cp_); MX_FENCE                                      \
+    MX_MFMA(3, 3, 0)                                                                        \
   }
 #define MX_ODD(ST, FULL)                                                                    \
   {                                                                                         \
@@ -567,22 +566,24 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     const StepRead rd_ = step_read(2 * st_ + 2);                                            \
     StageCopy cp_ = stage_copy(st_ + 2);                                                    \
     MX_FENCE                                                                                \
-    MX_MFMA(0, 0, 1) if (nx_) load_a(rd_, 0, 0); MX_FENCE                                   \
-    MX_MFMA(0, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(0, 2, 1) if (nx_) load_b(rd_, 0, 0); MX_FENCE                                   \
-    MX_MFMA(0, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(1, 0, 1) if (nx_) load_a(rd_, 0, 1); MX_FENCE                                   \
-    MX_MFMA(1, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(1, 2, 1) if (nx_) load_b(rd_, 0, 1); MX_FENCE                                   \
-    MX_MFMA(1, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(2, 0, 1) if (nx_) load_a(rd_, 0, 2); MX_FENCE                                   \
-    MX_MFMA(2, 1, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); MX_FENCE                                   \
-    MX_MFMA(2, 3, 1) if (pf_) copy_a(cp_); MX_FENCE                                      \
-    MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (sg_) scale_part(g_, 0); MX_FENCE       \
-    MX_MFMA(3, 1, 1) if (pf_) copy_a(cp_); if (sg_) scale_part(g_, 1); MX_FENCE          \
-    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (sg_) scale_part(g_, 2); MX_FENCE       \
-    MX_MFMA(3, 3, 1) if (pf_) copy_a(cp_); if (sg_) scale_part(g_, 3); MX_FENCE          \
+    MX_MFMA(0, 0, 1) if (nx_) load_a(rd_, 0, 0); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(0, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(0, 2, 1) if (nx_) load_b(rd_, 0, 0); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(0, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(1, 0, 1) if (nx_) load_a(rd_, 0, 1); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(1, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(1, 2, 1) if (nx_) load_b(rd_, 0, 1); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(1, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(2, 0, 1) if (nx_) load_a(rd_, 0, 2); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(2, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); if (pf_) copy_a(cp_); MX_FENCE             \
+    MX_MFMA(2, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
+    MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (pf_) copy_a(cp_);                      \
+    if (sg_) scale_part(g_, 0); MX_FENCE                                                    \
+    MX_MFMA(3, 1, 1) if (pf_) copy_b(cp_); if (sg_) scale_part(g_, 1); MX_FENCE             \
+    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (pf_) copy_a(cp_);                      \
+    if (sg_) scale_part(g_, 2); MX_FENCE                                                    \
+    MX_MFMA(3, 3, 1) if (pf_) copy_b(cp_); if (sg_) scale_part(g_, 3); MX_FENCE             \
   }
 
     // steady state (every stage has a successor two ahead), then the last

@@ -1,0 +1,201 @@
+"""Full-size parity of the hot path on the workloads of the benchmark table,
+in the launch configuration bench.py times (the same kernels and grids over
+the same sizes), checked on sampled outputs that the oracle computes one by
+one from the original bf16 inputs.
+
+Sampling (seeded): 128-row windows at the start of two experts for the
+forward and dgrad outputs (all the window's rows, 64 sampled columns); two
+32-wide column blocks for the column-wise copies and dbias (every token);
+64 x 64 sampled entries of every expert's weight gradient.  The oracle
+quantizes only what a sample needs: a window's rows, a 32-wide block of
+columns (a 1 x 32 block never crosses it), or one column of the weights for
+the column-wise weight copy.  Byte outputs are compared bit-exactly; GEMM
+outputs with the bounds of oracle.gemm (tolerance_f32 for forward and dgrad
+on Gaussian data, tolerance_mfma for wgrad and outlier data, bf16 within one
+ulp widened by the same allowance).  Properties that hold at any size are
+checked on whole outputs: a zero weight gradient for every expert without
+tokens.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import workloads as wl
+from oracle import gemm as og
+from oracle import mxfp8 as om
+
+from gpu_util import dev, f64, log, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(t):
+    """bf16 torch CPU tensor (any view) -> float64 numpy."""
+    return t.float().numpy().astype(np.float64)
+
+
+def _check(got, ref, mag, out_dtype, win=None):
+    tol = og.tolerance_f32(mag) if win is None else og.tolerance_mfma(mag, win)
+    if out_dtype == torch.float32:
+        err = np.abs(got - ref)
+        bad = err > tol
+        assert not bad.any(), (int(bad.sum()), float((err / tol).max()))
+    else:
+        ok = og.within_bf16_ulp(got, ref, tol)
+        assert ok.all(), int((~ok).sum())
+
+
+def _offsets(splits):
+    return np.concatenate([[0], np.cumsum(splits)]).astype(np.int64)
+
+
+def _window_experts(splits, rng):
+    """Two experts with at least 128 tokens: the largest and a random other."""
+    big = [g for g, m in enumerate(splits) if m >= 128]
+    first = int(np.argmax(splits))
+    rest = [g for g in big if g != first]
+    return [first] + ([int(rng.choice(rest))] if rest else [])
+
+
+def _run_linear(w, out_dtype):
+    """The hot path of one expert linear on the GPU, as bench.py runs it."""
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    ms = dev(w.m_splits)
+    x = w.tensors["x"].to("cuda")
+    wt = w.tensors["w"].to("cuda")
+    dy = w.dy.to("cuda")
+    log(f"full-size {w.name}: quantize")
+    xo = mx.group_quantize(x, mx.ROWWISE)
+    wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE)
+    log(f"full-size {w.name}: forward")
+    y = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
+                        out_dtype)
+    xc = mx.requant_colwise(xo.row_data, xo.row_scale)
+    log(f"full-size {w.name}: backward")
+    dyo = mx.group_quantize(dy, mx.ROWWISE)
+    dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True)
+    dx = mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n,
+                         k, out_dtype)
+    dw = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t,
+                         n, k, out_dtype)
+    torch.cuda.synchronize()
+    del x, wt, dy
+    return dict(xo=xo, wo=wo, y=y, xc=xc, dyo=dyo, dyc=dyc, db=db, dx=dx, dw=dw)
+
+
+def _check_linear(w, r, out_dtype, outliers, seed):
+    rng = np.random.default_rng(seed)
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    splits = [int(v) for v in w.m_splits]
+    offs = _offsets(splits)
+    x_t, w_t, dy_t = w.tensors["x"], w.tensors["w"], w.dy
+
+    # forward and dgrad on 128-row windows
+    for e in _window_experts(splits, rng):
+        rows = slice(int(offs[e]), int(offs[e]) + 128)
+        one = [128 if gi == e else 0 for gi in range(g)]
+        xq, xs = om.quantize_rowwise(_bf(x_t[rows]))
+        assert np.array_equal(u8(r["xo"].row_data[rows]), xq), f"X rows of expert {e}"
+        assert np.array_equal(u8(r["xo"].row_scale[rows]), xs)
+        cols = np.sort(rng.choice(n, size=64, replace=False))
+        wq, ws = om.quantize_rowwise(_bf(w_t[e][torch.from_numpy(cols)]))
+        assert np.array_equal(u8(r["wo"].row_data[e * n + torch.from_numpy(cols).cuda()]), wq)
+        ref, mag, win = og.fprop(xq, xs, wq[None], ws[None], [128], True, True)
+        log(f"full-size {w.name}: forward rows of expert {e}")
+        _check(f64(r["y"][rows][:, torch.from_numpy(cols).cuda()]), ref, mag, out_dtype,
+               win if outliers else None)
+
+        dyq, dys = om.quantize_rowwise(_bf(dy_t[rows]))
+        assert np.array_equal(u8(r["dyo"].row_data[rows]), dyq), f"dY rows of expert {e}"
+        kcols = np.sort(rng.choice(k, size=64, replace=False))
+        # column-wise weight copy [K, G*N]: for each sampled k, 32-blocks along G*N
+        wcol = _bf(w_t[:, :, torch.from_numpy(kcols)].reshape(g * n, kcols.size))
+        wcq, wcs = om.quantize_colwise(wcol, [g * n])
+        assert np.array_equal(u8(r["wo"].col_data[torch.from_numpy(kcols).cuda()]), wcq)
+        assert np.array_equal(u8(r["wo"].col_scale[torch.from_numpy(kcols).cuda()]), wcs)
+        ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, one, g, True)
+        log(f"full-size {w.name}: dgrad rows of expert {e}")
+        _check(f64(r["dx"][rows][:, torch.from_numpy(kcols).cuda()]), ref2, mag2, out_dtype)
+
+    # column-wise copies and dbias on two 32-wide column blocks (all tokens)
+    kb = np.sort(rng.choice(k // 32, size=2, replace=False))
+    nb = np.sort(rng.choice(n // 32, size=2, replace=False))
+    xcq, xcs, dycq, dycs = [], [], [], []
+    for b in kb:
+        q, s = om.quantize_rowwise(_bf(x_t[:, b * 32:(b + 1) * 32]))
+        cq, cs = om.requant_colwise(q, s, splits)
+        assert np.array_equal(u8(r["xc"].col_data[b * 32:(b + 1) * 32]), cq), f"X col block {b}"
+        assert np.array_equal(u8(r["xc"].col_scale[b * 32:(b + 1) * 32]), cs)
+        xcq.append(cq)
+        xcs.append(cs)
+    for b in nb:
+        q, s = om.quantize_rowwise(_bf(dy_t[:, b * 32:(b + 1) * 32]))
+        cq, cs = om.requant_colwise(q, s, splits)
+        assert np.array_equal(u8(r["dyc"].col_data[b * 32:(b + 1) * 32]), cq), f"dY col block {b}"
+        assert np.array_equal(u8(r["dyc"].col_scale[b * 32:(b + 1) * 32]), cs)
+        dycq.append(cq)
+        dycs.append(cs)
+        refb = om.grouped_dbias(q, s, splits)
+        absd = np.abs(om.dequantize_rowwise(q, s))
+        got = f64(r["db"][:, b * 32:(b + 1) * 32])
+        for gi in range(g):
+            magb = absd[offs[gi]:offs[gi + 1]].sum(axis=0)
+            assert np.all(np.abs(got[gi] - refb[gi]) <= og.tolerance_f32(magb)), f"dbias {gi}"
+
+    # weight gradient: 64 x 64 entries of every expert
+    ref3, mag3, win3 = og.wgrad(np.concatenate(dycq), np.concatenate(dycs),
+                                np.concatenate(xcq), np.concatenate(xcs), splits, True, True)
+    nsel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in nb])).cuda()
+    ksel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in kb])).cuda()
+    log(f"full-size {w.name}: wgrad samples")
+    _check(f64(r["dw"][:, nsel][:, :, ksel]), ref3, mag3, out_dtype, win3)
+    for gi, m in enumerate(splits):
+        if m == 0:
+            assert torch.count_nonzero(r["dw"][gi]).item() == 0, f"expert {gi} has no tokens"
+
+
+@pytest.mark.parametrize("name,seed", [("moe8_h4096_f14336", 21), ("skewed_dsv3", 22),
+                                       ("nemotron_proxy_mlp", 23)])
+def test_fullsize_linear(name, seed):
+    """cfg2 (the benchmark step), cfg4 (128 experts, 38 without tokens, X
+    outliers) and the FC1 linear of cfg3 (bf16 outputs)."""
+    w = wl.make(name)
+    if w.tensors["dy"].shape[1] != w.ffn:   # fused-MLP workloads carry the FC2 gradient
+        w.dy = wl.bf16_normal([w.wid, wl.STREAM_DY, 99], (w.tokens, w.ffn))
+    else:
+        w.dy = w.tensors["dy"]
+    w.name = name
+    out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    r = _run_linear(w, out_dtype)
+    _check_linear(w, r, out_dtype, outliers=(name == "skewed_dsv3"), seed=seed)
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_group_quantize():
+    """cfg5: row + column-wise quantize of 131072 x 7168 t(3) values with 1 %
+    zero tiles, 256 experts (43 without tokens)."""
+    name = "group_quantize_131072x7168"
+    w = wl.make(name)
+    t, k = w.tokens, w.hidden
+    splits = [int(v) for v in w.m_splits]
+    rng = np.random.default_rng(24)
+    log(f"full-size {name}: quantize")
+    xo = mx.group_quantize(w.tensors["x"].to("cuda"), mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(t, size=256, replace=False))
+    q, s = om.quantize_rowwise(_bf(w.tensors["x"][torch.from_numpy(rows)]))
+    sel = torch.from_numpy(rows).cuda()
+    assert np.array_equal(u8(xo.row_data[sel]), q) and np.array_equal(u8(xo.row_scale[sel]), s)
+    for b in np.sort(rng.choice(k // 32, size=3, replace=False)):
+        cq, cs = om.quantize_colwise(_bf(w.tensors["x"][:, b * 32:(b + 1) * 32]), splits)
+        assert np.array_equal(u8(xo.col_data[b * 32:(b + 1) * 32]), cq), f"col block {b}"
+        assert np.array_equal(u8(xo.col_scale[b * 32:(b + 1) * 32]), cs)
+    # the zero tiles quantize to code 0 with scale byte 0 (reading c2)
+    zero_rows = np.where((_bf(w.tensors["x"][:, :32]) == 0).all(axis=1))[0]
+    if zero_rows.size:
+        zr = torch.from_numpy(zero_rows[:64]).cuda()
+        assert torch.all(xo.row_scale[zr, 0] == 0)
+        assert torch.all((xo.row_data[zr, :32] & 0x7F) == 0)

@@ -56,6 +56,10 @@ CASES = [
     ([128, 256, 0, 384], 512, 512),
     ([512], 1024, 512),
     ([0, 128, 0, 0, 640, 128, 256, 0], 512, 1024),
+    # T = 128: fewer tokens than one 256-row tile (the upper waves copy rows
+    # of the lower ones; nothing past the last token is read or written)
+    ([128], 512, 512),
+    ([0, 128, 0], 512, 1536),
 ]
 
 
@@ -137,13 +141,19 @@ def test_rows_outside_experts_untouched():
 
 @pytest.mark.parametrize("name", ["tiny_fwd", "small_moe8", "small_skewed", "small_nemotron_mlp"])
 def test_workload_fwd_bwd(name):
-    """The hot path on a workload recipe: quantize, forward, requant, dgrad, wgrad."""
+    """The hot path on a workload recipe: quantize, forward, requant, dgrad,
+    wgrad, dbias.  Every oracle input is the oracle's own quantization of the
+    bf16 tensors; the GPU's bytes are checked equal to it stage by stage."""
     w = wl.make(name)
     g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
     out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
     outliers = "skewed" in name      # X carries 0.1 % outliers x1000
     ms = dev(w.m_splits)
     splits = [int(v) for v in w.m_splits]
+    x64 = w.tensors["x"].double().numpy()
+    w64 = w.tensors["w"].double().numpy().reshape(g * n, k)
+    xq, xs = om.quantize_rowwise(x64)
+    wq, ws = om.quantize_rowwise(w64)
     log(f"workload {name}: quantize")
     xo = mx.group_quantize(w.tensors["x"].to("cuda"), mx.ROWWISE)
     wo = mx.group_quantize(w.tensors["w"].to("cuda"), mx.ROWWISE | mx.COLWISE)
@@ -151,8 +161,8 @@ def test_workload_fwd_bwd(name):
     y = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
                         out_dtype)
     torch.cuda.synchronize()
-    xq, xs = u8(xo.row_data), u8(xo.row_scale)
-    wq, ws = u8(wo.row_data), u8(wo.row_scale)
+    assert np.array_equal(u8(xo.row_data), xq) and np.array_equal(u8(xo.row_scale), xs)
+    assert np.array_equal(u8(wo.row_data), wq) and np.array_equal(u8(wo.row_scale), ws)
     ref, mag, win = og.fprop(xq, xs, wq.reshape(g, n, k), ws.reshape(g, n, k // 32), splits,
                              True, True)
     _check(f64(y), ref, mag, out_dtype, win if outliers else None)
@@ -161,6 +171,8 @@ def test_workload_fwd_bwd(name):
     dy_t = w.tensors["dy"]
     if dy_t.shape[1] != n:     # fused-MLP workloads carry the FC2 gradient; use an FC1-shaped one
         dy_t = wl.bf16_normal([w.wid, wl.STREAM_DY, 99], (t, n))
+    dyq, dys = om.quantize_rowwise(dy_t.double().numpy())
+    wcq, wcs = om.quantize_colwise(w64, [g * n])
     log(f"workload {name}: backward")
     dyo = mx.group_quantize(dy_t.to("cuda"), mx.ROWWISE)
     xo2, _db_x = mx.requant_colwise(xo.row_data, xo.row_scale, ms, with_dbias=True)
@@ -170,16 +182,16 @@ def test_workload_fwd_bwd(name):
     dw = mx.grouped_gemm("TN", dyo2.col_data, dyo2.col_scale, xo2.col_data, xo2.col_scale, ms,
                          t, n, k, out_dtype)
     torch.cuda.synchronize()
-    dyq, dys = u8(dyo.row_data), u8(dyo.row_scale)
+    assert np.array_equal(u8(dyo.row_data), dyq) and np.array_equal(u8(dyo.row_scale), dys)
+    assert np.array_equal(u8(wo.col_data), wcq) and np.array_equal(u8(wo.col_scale), wcs)
     # column-wise copies: bit-exact against the oracle's requant
-    qc, sc = om.requant_colwise(dyq, dys, splits)
-    assert np.array_equal(u8(dyo2.col_data), qc) and np.array_equal(u8(dyo2.col_scale), sc)
-    qc, sc = om.requant_colwise(xq, xs, splits)
-    assert np.array_equal(u8(xo2.col_data), qc) and np.array_equal(u8(xo2.col_scale), sc)
-    ref2, mag2 = og.dgrad(dyq, dys, u8(wo.col_data), u8(wo.col_scale), splits, g, True)
+    dycq, dycs = om.requant_colwise(dyq, dys, splits)
+    assert np.array_equal(u8(dyo2.col_data), dycq) and np.array_equal(u8(dyo2.col_scale), dycs)
+    xcq, xcs = om.requant_colwise(xq, xs, splits)
+    assert np.array_equal(u8(xo2.col_data), xcq) and np.array_equal(u8(xo2.col_scale), xcs)
+    ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, splits, g, True)
     _check(f64(dx), ref2, mag2, out_dtype)
-    ref3, mag3, win3 = og.wgrad(u8(dyo2.col_data), u8(dyo2.col_scale), u8(xo2.col_data),
-                                u8(xo2.col_scale), splits, True, True)
+    ref3, mag3, win3 = og.wgrad(dycq, dycs, xcq, xcs, splits, True, True)
     # wgrad contracts over one expert's tokens (a few 128-element windows):
     # the window truncation does not average out, so it is gated on the
     # window bound even for Gaussian data
@@ -191,3 +203,5 @@ def test_workload_fwd_bwd(name):
         magb = xh[row:row + m].sum(axis=0)
         assert np.all(np.abs(f64(db)[gi] - refb[gi]) <= og.tolerance_f32(magb))
         row += m
+        if m == 0:
+            assert np.all(f64(dw)[gi] == 0)

@@ -97,7 +97,7 @@ def calibrate_copy():
           flush=True)
 
 
-def cpu_baseline(w, budget_rows=1024, n_cols=2048):
+def cpu_baseline(w, budget_rows=4096, n_cols=2048):
     """Time the CPU oracle on a bounded sample of the same workload.
 
     Sample: the first `budget_rows` tokens, re-split as 8 experts of 128 rows,

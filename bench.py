@@ -59,10 +59,15 @@ def parse():
 
 
 def gemm_source_hash():
+    """sha256 of the GEMM sources with comments and whitespace removed, so
+    that only a change of the code itself retires the stored counters."""
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()
 
 

@@ -23,8 +23,8 @@
 // inside every workgroup: no host synchronisation, and an expert with no
 // tokens owns no forward/dgrad tile and a zero wgrad output.
 //
-// Kernel structure (one 256 x 256 output tile per workgroup, 4 waves of
-// 128 x 128):
+// Kernel structure (persistent: one workgroup per CU walks 256 x 256 output
+// tiles; 4 waves of 128 x 128):
 //  * MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4, both operands E4M3.  Lane l
 //    (row l % 32 of the operand, half g = l / 32) supplies the contraction
 //    bytes [16g, 16g+16) and [32+16g, 32+16g+16) of a 64-byte step, and the
@@ -33,14 +33,14 @@
 //  * The MFMA's first operand is the A tile and its second the B tile, so the
 //    32 lanes of a half-wave hold 32 consecutive output columns of one row:
 //    a store of one accumulator register writes whole cache lines.
-//  * Stages of 64 contraction bytes go HBM/L2 -> LDS by LDS DMA (no register
-//    staging) into a ring of 4 buffers, so three stages are in flight while
-//    one is consumed.  Each wave copies a quarter of every stage; a stage is
-//    read only after every wave has waited for its own copies and passed a
-//    barrier.
-//  * Inside a step, the next A fragment is read while the current one's 4
-//    MFMAs run; the barrier sits before the last MFMA group so that the next
-//    stage's B fragments are read while that group runs.
+//  * Operands go HBM/L2 -> LDS by LDS DMA (no register staging), one whole
+//    128-byte line per row: an LDS stage holds 128 contraction bytes (two
+//    MFMA steps) of the 256 A and 256 B rows, in two slots; E8M0 scales in
+//    groups of 8 steps.
+//  * The fragments of the next step are read into a second register set
+//    while the current step's MFMAs run, one read per MFMA.  Odd steps open
+//    with the only wait and barrier, then interleave the copies of the stage
+//    two ahead with their MFMAs.
 #include <algorithm>
 
 #include "mx_device.h"

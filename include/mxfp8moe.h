@@ -210,6 +210,26 @@ mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t*
 mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                               uint16_t* dh, void* stream);
 
+/*
+ * mxfp8_convert_sweep -- diagnostic: runs the device's E4M3 / E8M0 conversion
+ * helpers (the ones every quantize kernel encodes and decodes with) over
+ * every (value, scale byte) pair, so that a test can compare them with an
+ * independent encoder (OCP Microscaling Formats v1.0, sections 5.3-5.4 and
+ * 6.3: E4M3 round to nearest even, saturated to 448; value = code * 2^X).
+ * Not a step of the hot path.
+ *   mode 0: out holds 2^24 u16; entry 65536 * s + h = the codes of the bf16
+ *           values (h, h ^ 0x8000) encoded with scale byte s (byte 0 is h).
+ *   mode 1: out holds 2^24 u8; entry 65536 * x + 256 * s + c = code c decoded
+ *           with scale byte s and encoded again with scale byte x.
+ *   mode 2: out holds 2^16 pairs of fp32 bit patterns; entry 256 * s + c =
+ *           the codes (c, c ^ 0x80) decoded with scale byte s.
+ * out: device buffer of at least mxfp8_convert_sweep_bytes(mode) bytes,
+ * written asynchronously on `stream`.  Errors: EINVAL for an unknown mode, a
+ * NULL or too small buffer.
+ */
+size_t mxfp8_convert_sweep_bytes(int32_t mode);
+mxfp8_status mxfp8_convert_sweep(int32_t mode, void* out, size_t out_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -249,3 +249,16 @@ def swiglu_bwd(h, da, out=None, stream=None):
     _native.check(lib.mxfp8_swiglu_bwd(_ptr(h), _ptr(da), t, f, _ptr(out), _stream(stream)),
                   "mxfp8_swiglu_bwd")
     return out
+
+
+def convert_sweep(mode, stream=None):
+    """Diagnostic: the device conversion helpers over every (value, scale byte)
+    pair (layouts in mxfp8_convert_sweep's header comment); a uint8 tensor."""
+    lib = _lib()
+    need = lib.mxfp8_convert_sweep_bytes(mode)
+    if need == 0:
+        raise ValueError(f"unknown sweep mode {mode}")
+    out = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = lib.mxfp8_convert_sweep(mode, _ptr(out), need, _stream(stream))
+    _native.check(st, "mxfp8_convert_sweep")
+    return out

@@ -198,4 +198,16 @@ mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, 
   return hip_status(mx::launch_swiglu_bwd(h, da, T, F, dh, as_stream(stream)), fn);
 }
 
+size_t mxfp8_convert_sweep_bytes(int32_t mode) { return mx::convert_sweep_bytes(mode); }
+
+mxfp8_status mxfp8_convert_sweep(int32_t mode, void* out, size_t out_bytes, void* stream) {
+  const char* fn = "mxfp8_convert_sweep";
+  const size_t need = mx::convert_sweep_bytes(mode);
+  REQUIRE(need != 0, "%s: unknown mode %d", fn, (int)mode);
+  REQUIRE(out != nullptr && out_bytes >= need, "%s: mode %d needs a buffer of %zu bytes", fn,
+          (int)mode, need);
+  return hip_status(mx::launch_convert_sweep(mode, static_cast<uint8_t*>(out), as_stream(stream)),
+                    fn);
+}
+
 }  // extern "C"

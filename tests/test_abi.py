@@ -108,6 +108,16 @@ def test_swiglu_and_validate_reject(lib):
     assert lib.mxfp8_validate_splits(FAKE, 1, 128, None, None) == 1
 
 
+def test_convert_sweep_sizes_and_rejects(lib):
+    assert lib.mxfp8_convert_sweep_bytes(0) == 2 << 24
+    assert lib.mxfp8_convert_sweep_bytes(1) == 1 << 24
+    assert lib.mxfp8_convert_sweep_bytes(2) == 8 << 16
+    assert lib.mxfp8_convert_sweep_bytes(3) == 0
+    assert lib.mxfp8_convert_sweep(3, FAKE, 1 << 30, None) == 1
+    assert lib.mxfp8_convert_sweep(0, FAKE, (2 << 24) - 1, None) == 1
+    assert lib.mxfp8_convert_sweep(2, None, 1 << 20, None) == 1
+
+
 def test_binding_maps_errors(lib):
     with pytest.raises(ValueError):
         _native.check(1, "x")

@@ -144,6 +144,28 @@ def test_requant_wide_scales():
     _requant_case(q, s, splits, 7)
 
 
+def test_requant_scale_bytes_above_fast_range():
+    """Row scale bytes 247..254 (beyond what bf16 data produces) decode past
+    the fp32 range, so the kernel requantizes such tiles with its integer
+    path; tiles 0 and 2 of the 128-row tiles hold such bytes, tile 1 does not."""
+    rng = np.random.default_rng(13)
+    q, s = random_mx(rng, 384, 512, smin=100, smax=246)
+    s[:128, :4] = rng.integers(247, 255, size=(128, 4))       # tile (0, 0): every row
+    s[300, 9] = 254                                           # tile (2, 2): one byte
+    log("requant with scale bytes 247..254")
+    out = mx.requant_colwise(dev(q), dev(s))
+    torch.cuda.synchronize()
+    qc, sc = om.requant_colwise(q, s, [384])
+    assert np.array_equal(u8(out.col_scale), sc)
+    assert np.array_equal(u8(out.col_data), qc)
+    # with dbias: values small enough that the fp32 sums stay finite (codes
+    # <= 3 * 2^-9 under the bytes above 246, other bytes at most 200)
+    q2, s2 = q.copy(), np.where(s > 246, s, np.minimum(s, 200)).astype(np.uint8)
+    q2[:128, :128] &= 0x83
+    q2[300, 288:320] &= 0x83
+    _requant_case(q2, s2, [128, 256], 13)
+
+
 def test_requant_of_quantized_sweep():
     x = bf16_from_bits(sweep_bf16_bits(512, 512, 9))
     q, s = om.quantize_rowwise(f64(x))

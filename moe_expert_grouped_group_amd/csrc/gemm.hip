@@ -163,6 +163,32 @@ __device__ __forceinline__ const uint8_t* opaque_ptr(const uint8_t* q) {
   return q;
 }
 
+// 4 x 4 transpose inside each quad of lanes: on entry lane q of the quad
+// holds element (row r, column q) of a block in v_r; on exit lane q holds
+// (row q, column r) in v_r.  Two exchange rounds (lanes q ^ 1, then q ^ 2),
+// each swapping the off-diagonal 2 x 2 entries through a DPP quad permutation.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_xor) {
+  const int ctrl = ctrl_xor == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __int_as_float(ctrl == 0xB1
+      ? __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)
+      : __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void quad_transpose(float& v0, float& v1, float& v2, float& v3,
+                                               bool odd, bool hi2) {
+  float y = dpp_f(odd ? v0 : v1, 1);
+  v0 = odd ? y : v0;
+  v1 = odd ? v1 : y;
+  y = dpp_f(odd ? v2 : v3, 1);
+  v2 = odd ? y : v2;
+  v3 = odd ? v3 : y;
+  y = dpp_f(hi2 ? v0 : v2, 2);
+  v0 = hi2 ? y : v0;
+  v2 = hi2 ? v2 : y;
+  y = dpp_f(hi2 ? v1 : v3, 2);
+  v1 = hi2 ? y : v1;
+  v3 = hi2 ? v3 : y;
+}
+
 // Expert table kept in LDS for the whole launch: exclusive prefix of tiles
 // (forward/dgrad: ceil(M_g / BM) row tiles per expert) and of token rows, and
 // (wgrad) the experts in decreasing order of tokens.
@@ -499,7 +525,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      const StepRead r0 = step_read(0);
+      // step 0 through an opaque index: with constant offsets its addresses
+      // would be precomputed once and spilled, and the reload's wait counts
+      // every copy and store in flight
+      const StepRead r0 = step_read((int)opaque(0u));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         load_a(r0, 0, i);
@@ -551,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     MX_MFMA(3, 2, 0) load_b(rd_, 1, 3); MX_FENCE                                            \
     MX_MFMA(3, 3, 0)                                                                        \
   }
-#define MX_ODD(ST, FULL)                                                                    \
+#define MX_ODD(ST, FULL)                                                                         \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
     const bool nx_ = (FULL) || st_ + 1 < ns;                                                \
@@ -616,18 +645,27 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       tile_prologue(nxt.nk);
     }
 
+    // The epilogue's tile bounds and output base are recomputed from the
+    // expert table (LDS) rather than kept from the tile start: held across
+    // the K loop they are spilled, and the reload's wait on the vector memory
+    // counter would also wait for the next tile's copies issued above.
+    const TileDesc ed = describe<KGROUPED>(p, &table, tile, esz);
+
     // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
-    // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32,
-    // so one store instruction per register writes 32 consecutive columns of
-    // two rows: whole 128-byte lines for fp32 output.  The row part of the
-    // address is wave-uniform (scalar base); the lane part is a 32-bit offset.
-    // Global (not generic) stores: a generic store also counts on the LDS
-    // wait counter, which the loop waits on for its fragment reads.
-    {
+    // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32.
+    // The row part of each store address is wave-uniform (scalar base), the
+    // lane part a 32-bit offset.  Global (not generic) stores: a generic store
+    // also counts on the LDS wait counter, which the loop waits on for its
+    // fragment reads.
+    // Forward and dgrad (long contractions): one store instruction per
+    // register writes 32 consecutive columns of two rows, whole 128-byte
+    // lines for fp32 output.  (The 16-byte form below measured 2 % slower
+    // here: its transposes cost more than the store instructions it saves.)
+    if (!KGROUPED) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
       const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (int64_t)(wn * WT + fr) * esz);
-      const int lo = cur.row_lo, hi = cur.row_hi;
+      const int lo = ed.row_lo, hi = ed.row_hi;
       const bool part = lo > 0 || hi < BM;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -635,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
           if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
-          char* rbase = cur.c + (int64_t)row * ldc_b + lane_off;
+          char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (OUT_BF16)
@@ -643,6 +681,61 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
                   (uint16_t)f32_to_bf16(acc[i][j][r]);
             else
               *(__attribute__((address_space(1))) float*)(rbase + j * 32 * 4) = acc[i][j][r];
+          }
+        }
+      }
+    }
+    // wgrad (one expert's tokens: short contractions, so the epilogue weighs
+    // more; 6 % faster than one register per store).
+    // Registers 4b..4b+3 of a quad of lanes (4 consecutive columns) hold a
+    // 4 x 4 block of C; a DPP transpose inside the quad leaves lane q of it
+    // with row 8b + 4 (l/32) + q, its 4 columns in registers 0..3, so one
+    // 16-byte store per 4 registers writes, per instruction, 8 rows of 32
+    // consecutive columns: whole 128-byte lines (fp32), 4x fewer store
+    // instructions than one register at a time.  The row part of the address
+    // is wave-uniform (scalar base); the lane part is a 32-bit offset.
+    else {
+      const int64_t ldc_b = p.ldc * esz;
+      const int wm_u = __builtin_amdgcn_readfirstlane(wm);
+      // per-lane values derived here from the hardware lane id (volatile
+      // mbcnt, so it is not hoisted): from a value computed at the kernel
+      // entry they would stay live through the K loop, where no register is
+      // left
+      uint32_t ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const uint32_t q4 = ln & 3;               // row of the 4 x 4 block after the transpose
+      const uint32_t cq = (ln & 31) >> 2;       // column quad of the 32-column fragment
+      const bool odd = (ln & 1) != 0, hi2 = (ln & 2) != 0;
+      const uint32_t my_row = 4 * (ln >> 5) + q4;   // within an 8-row group
+      // 32-bit lane offset (7 rows of at most a few hundred KB plus a column)
+      const uint32_t lane_off =
+          my_row * (uint32_t)ldc_b + (uint32_t)(wn * WT) * (uint32_t)esz + 4 * cq * (uint32_t)esz;
+      const int lo = ed.row_lo, hi = ed.row_hi;
+      const bool part = lo > 0 || hi < BM;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
+          const bool ok = !part || (row + (int)my_row >= lo && row + (int)my_row < hi);
+          // scalar row base + 32-bit lane offset (the scalar-base store form)
+          char* rbase = (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
+            float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
+            quad_transpose(v0, v1, v2, v3, odd, hi2);
+            if (!ok) continue;
+            if (OUT_BF16) {
+              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+              *(__attribute__((address_space(1))) u32x2*)(rbase + j * 32 * 2) =
+                  u32x2{f32_to_bf16(v0) | (f32_to_bf16(v1) << 16),
+                        f32_to_bf16(v2) | (f32_to_bf16(v3) << 16)};
+            } else {
+              typedef float f32x4 __attribute__((ext_vector_type(4)));
+              *(__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4) =
+                  f32x4{v0, v1, v2, v3};
+            }
           }
         }
       }

@@ -227,6 +227,28 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
 
     per = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
+
+    # Outside the step: wgrad accumulated into an fp32 main_grad (the
+    # production form of the wgrad launch), timed on the same operands.
+    acc_ms = None
+    if out_dtype == torch.float32:
+        main_grad = torch.zeros(g, n, k, dtype=torch.float32, device=dev)
+        acc = lambda: mx.grouped_gemm_wgrad_accumulate(  # noqa: E731
+            dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, main_grad)
+        for _ in range(2):
+            acc()
+        torch.cuda.synchronize()
+        pairs = []
+        for _ in range(max(args.steps, 3)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            acc()
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        acc_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+        del main_grad
     flop_one = 2.0 * t * n * k
     gemm_ms = per["gemm_fprop"] + per["gemm_dgrad"] + per["gemm_wgrad"]
     gemm_tflops = 3 * flop_one / (gemm_ms * 1e-3) / 1e12
@@ -262,6 +284,9 @@ def main():
         "gemm_tflops": round(gemm_tflops, 2),
         "group_quantize_gbs": round(quant_gbs, 1),
         "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
+        "wgrad_accumulate": None if acc_ms is None else {
+            "ms": round(acc_ms, 4), "tflops": round(flop_one / (acc_ms * 1e-3) / 1e12, 2),
+            "note": "main_grad += dY^T X in fp32, outside the step"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),

@@ -183,6 +183,27 @@ mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uin
                                 const int64_t* m_splits, int32_t G, void* stream);
 
 /*
+ * mxfp8_grouped_gemm_wgrad_accumulate -- the TN (wgrad) product of
+ * mxfp8_grouped_gemm added into an existing fp32 weight-gradient buffer
+ * instead of overwriting it, the form a training step uses when the weight
+ * gradient accumulates into an fp32 main_grad ([P3545] last commit message:
+ * the fused grouped MLP's weight gradients are checked in main_grad):
+ *      main_grad[g] += sum over r in expert g of dY[r]^T X[r]
+ *  a, b, T, N, K, m_splits, G as for the TN layout of mxfp8_grouped_gemm;
+ *  main_grad: caller-owned device fp32 [G, N, K], read and written.  The sum
+ *  of an expert's product is formed in fp32 as for mxfp8_grouped_gemm and
+ *  added to main_grad once (one fp32 rounding).  An expert with no rows
+ *  leaves its main_grad[g] untouched (bit for bit).
+ * Errors: EINVAL for NULL pointers, T % 128, N % 512, K % 512, G < 1 or
+ * G > 1024, host m_splits.
+ */
+mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const uint8_t* a_scale,
+                                                 const uint8_t* b_data, const uint8_t* b_scale,
+                                                 float* main_grad, int64_t T, int64_t N, int64_t K,
+                                                 const int64_t* m_splits, int32_t G,
+                                                 void* stream);
+
+/*
  * mxfp8_validate_splits -- device-side check of the alignment contract on the
  * device splits ([P3224] review: an alignment check must accompany device
  * m_splits).  Writes *flag (device int32) = bitmask: 1 = a negative split,

@@ -32,6 +32,8 @@ SIGNATURES = {
     "mxfp8_grouped_gemm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64,
                                    c_i64, c_vp, c_i32, c_vp]),
     "mxfp8_validate_splits": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp]),
+    "mxfp8_grouped_gemm_wgrad_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                    c_i64, c_vp, c_i32, c_vp]),
     "mxfp8_swiglu_fwd": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "mxfp8_swiglu_bwd": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "mxfp8_convert_sweep_bytes": (c_size, [c_i32]),

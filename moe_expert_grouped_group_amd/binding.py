@@ -211,6 +211,27 @@ def grouped_gemm(layout, a_data, a_scale, b_data, b_scale, m_splits, tokens, n, 
     return out
 
 
+def grouped_gemm_wgrad_accumulate(a_data, a_scale, b_data, b_scale, m_splits, tokens, n, k,
+                                  main_grad, stream=None):
+    """wgrad added into an fp32 main_grad [G, n, k] in place:
+    main_grad[g] += dY_g^T X_g (a = dY column-wise [n, T], b = X column-wise
+    [k, T]); experts without tokens keep their main_grad untouched."""
+    lib = _lib()
+    ms = _splits(m_splits)
+    g = ms.numel()
+    t = tokens
+    a2 = _as_shape(a_data, (n, t), "a_data")
+    as2 = _as_shape(a_scale, (n, t // 32), "a_scale")
+    b2 = _as_shape(b_data, (k, t), "b_data")
+    bs2 = _as_shape(b_scale, (k, t // 32), "b_scale")
+    _need(main_grad, torch.float32, (g, n, k), "main_grad")
+    st = lib.mxfp8_grouped_gemm_wgrad_accumulate(_ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2),
+                                                 _ptr(main_grad), t, n, k, _ptr(ms), g,
+                                                 _stream(stream))
+    _native.check(st, "mxfp8_grouped_gemm_wgrad_accumulate")
+    return main_grad
+
+
 def validate_splits(m_splits, tokens, flag=None, stream=None):
     """Enqueue the device-side split check; returns the device int32 flag tensor."""
     lib = _lib()

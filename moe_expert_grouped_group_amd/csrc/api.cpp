@@ -164,7 +164,29 @@ mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uin
   if (T == 0 && layout != MXFP8_LAYOUT_TN) return ok();
   const hipError_t e = mx::launch_grouped_gemm(layout, a_data, a_scale, b_data, b_scale, c,
                                                c_dtype == MXFP8_OUT_BF16, T, N, K, m_splits, G,
-                                               as_stream(stream));
+                                               false, as_stream(stream));
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const uint8_t* a_scale,
+                                                 const uint8_t* b_data, const uint8_t* b_scale,
+                                                 float* main_grad, int64_t T, int64_t N, int64_t K,
+                                                 const int64_t* m_splits, int32_t G,
+                                                 void* stream) {
+  const char* fn = "mxfp8_grouped_gemm_wgrad_accumulate";
+  REQUIRE(a_data && a_scale && b_data && b_scale && main_grad, "%s: NULL pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
+          (long long)N);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  REQUIRE(G <= 1024, "%s: G = %d exceeds the supported 1024 experts", fn, (int)G);
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  if (T == 0) return ok();   // every expert is empty: main_grad stays as it is
+  const hipError_t e =
+      mx::launch_grouped_gemm(MXFP8_LAYOUT_TN, a_data, a_scale, b_data, b_scale, main_grad, false,
+                              T, N, K, m_splits, G, true, as_stream(stream));
   return hip_status(e, fn);
 }
 

@@ -343,7 +343,8 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
   return d;
 }
 
-template <bool KGROUPED, bool OUT_BF16>
+// ACCUM (wgrad with fp32 output only): C += the product instead of C = it.
+template <bool KGROUPED, bool OUT_BF16, bool ACCUM = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
@@ -686,7 +687,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       }
     }
     // wgrad (one expert's tokens: short contractions, so the epilogue weighs
-    // more; 6 % faster than one register per store).
+    // more; 6 % faster than one register per store).  Accumulating into C,
+    // an expert without tokens (nk == 0) leaves its C untouched, and the old
+    // values are loaded 16 at a time (one 4-row block of every fragment)
+    // before they are added: the wait for a load also waits for every store
+    // issued before it, so loading one value at a time would serialise.
     // Registers 4b..4b+3 of a quad of lanes (4 consecutive columns) hold a
     // 4 x 4 block of C; a DPP transpose inside the quad leaves lane q of it
     // with row 8b + 4 (l/32) + q, its 4 columns in registers 0..3, so one
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // consecutive columns: whole 128-byte lines (fp32), 4x fewer store
     // instructions than one register at a time.  The row part of the address
     // is wave-uniform (scalar base); the lane part is a 32-bit offset.
-    else {
+    else if (!ACCUM || nk > 0) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
       // per-lane values derived here from the hardware lane id (volatile
@@ -712,8 +717,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
           my_row * (uint32_t)ldc_b + (uint32_t)(wn * WT) * (uint32_t)esz + 4 * cq * (uint32_t)esz;
       const int lo = ed.row_lo, hi = ed.row_hi;
       const bool part = lo > 0 || hi < BM;
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        f32x4 old[4][4];
+        if (ACCUM) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int row = wm_u * WT + 32 * i + 8 * b;
+            const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              old[b][j] = *(__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4);
+          }
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
@@ -725,6 +742,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
             float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
             float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
             quad_transpose(v0, v1, v2, v3, odd, hi2);
+            if (ACCUM) {
+              v0 += old[b][j].x;
+              v1 += old[b][j].y;
+              v2 += old[b][j].z;
+              v3 += old[b][j].w;
+            }
             if (!ok) continue;
             if (OUT_BF16) {
               typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -732,7 +755,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
                   u32x2{f32_to_bf16(v0) | (f32_to_bf16(v1) << 16),
                         f32_to_bf16(v2) | (f32_to_bf16(v3) << 16)};
             } else {
-              typedef float f32x4 __attribute__((ext_vector_type(4)));
               *(__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4) =
                   f32x4{v0, v1, v2, v3};
             }
@@ -746,15 +768,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   }
 }
 
-template <bool KG, bool BF>
+template <bool KG, bool BF, bool ACC = false>
 static hipError_t launch_one(const GemmArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<KG, BF>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<KG, BF, ACC>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                const uint8_t* sb, void* c, bool out_bf16, int64_t T, int64_t N,
-                               int64_t K, const int64_t* m_splits, int32_t G, hipStream_t st) {
+                               int64_t K, const int64_t* m_splits, int32_t G, bool accumulate,
+                               hipStream_t st) {
   GemmArgs p{};
   p.a = a;
   p.sa = sa;
@@ -797,6 +820,7 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+  if (kgrouped && accumulate) return launch_one<true, false, true>(p, grid, st);
   if (kgrouped)
     return out_bf16 ? launch_one<true, true>(p, grid, st) : launch_one<true, false>(p, grid, st);
   return out_bf16 ? launch_one<false, true>(p, grid, st) : launch_one<false, false>(p, grid, st);

@@ -146,6 +146,28 @@ def wgrad(dycq, dycs, xcq, xcs, m_splits, magnitude=False, window=False):
     return _ret(out, mag, win)
 
 
+def wgrad_accumulate(main_grad, dycq, dycs, xcq, xcs, m_splits, magnitude=False, window=False):
+    """main_grad[g] + dY_g^T X_g: the wgrad product added into an fp32 weight
+    gradient buffer, the form in which the fused grouped MLP's weight
+    gradients are produced ("[PyTorch] Fix distributed BF16 weights and trim
+    NVFP4 saved state in the fused grouped MLP", last commit message: the
+    regression tests compare the main_grad wgrads).  An expert with no rows
+    keeps its main_grad[g] exactly as it is (also the sign of a zero).
+
+    main_grad: float32 [G, N, K].  Returns float64 [G, N, K] (and the
+    magnitudes / window maxima of the product, as wgrad).
+    """
+    res = wgrad(dycq, dycs, xcq, xcs, m_splits, magnitude, window)
+    prod = res[0] if isinstance(res, tuple) else res
+    base = np.asarray(main_grad, dtype=np.float32).astype(np.float64)
+    m, _ = _splits(m_splits, np.asarray(dycq).shape[1])
+    out = base + prod
+    for g in range(len(m)):
+        if m[g] == 0:
+            out[g] = base[g]
+    return (out,) + tuple(res[1:]) if isinstance(res, tuple) else out
+
+
 def _ret(out, mag, win):
     res = (out,) + ((mag,) if mag is not None else ()) + ((win,) if win is not None else ())
     return res if len(res) > 1 else out

@@ -108,6 +108,14 @@ def test_swiglu_and_validate_reject(lib):
     assert lib.mxfp8_validate_splits(FAKE, 1, 128, None, None) == 1
 
 
+def test_wgrad_accumulate_rejects(lib):
+    f = lib.mxfp8_grouped_gemm_wgrad_accumulate
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 128, 512, 512, FAKE, 1, None) == 1      # no main_grad
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 512, 512, FAKE, 1, None) == 1      # T % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 500, 512, FAKE, 1, None) == 1      # N % 512
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 2000, None) == 1   # G > 1024
+
+
 def test_convert_sweep_sizes_and_rejects(lib):
     assert lib.mxfp8_convert_sweep_bytes(0) == 2 << 24
     assert lib.mxfp8_convert_sweep_bytes(1) == 1 << 24

@@ -105,6 +105,45 @@ def test_three_layouts_synthetic(kind, case, out_dtype):
             assert np.all(f64(dw)[gi] == 0)
 
 
+@pytest.mark.parametrize("kind", ["random", "integer"])
+@pytest.mark.parametrize("case", [0, 2, 4])
+def test_wgrad_accumulate(kind, case):
+    """main_grad[g] += dY_g^T X_g in place.  Bound: the wgrad bound of the
+    product plus one fp32 rounding of the final sum (2^-24 of its size);
+    integer-valued data is exact.  Experts without tokens keep their slice
+    bit for bit (their base holds negative zeros, which an added +0 would
+    turn positive)."""
+    splits, n, k = CASES[case]
+    g = len(splits)
+    t = sum(splits)
+    rng = np.random.default_rng(2000 + case)
+    dycq, dycs = _mx_rows(rng, n, t, kind)
+    xcq, xcs = _mx_rows(rng, k, t, kind)
+    if kind == "integer":
+        base = rng.integers(-64, 65, size=(g, n, k)).astype(np.float32)
+    else:
+        base = (rng.standard_normal((g, n, k)) * 100).astype(np.float32)
+    for gi, m in enumerate(splits):
+        if m == 0:
+            base[gi, ::3] = -0.0
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    mg = dev(base)
+    log(f"wgrad accumulate {kind} case {case}")
+    mx.grouped_gemm_wgrad_accumulate(dev(dycq), dev(dycs), dev(xcq), dev(xcs), ms, t, n, k, mg)
+    torch.cuda.synchronize()
+    got = mg.cpu().numpy()
+    ref, mag, win = og.wgrad_accumulate(base, dycq, dycs, xcq, xcs, splits, True, True)
+    for gi, m in enumerate(splits):
+        if m == 0:
+            assert np.array_equal(got[gi].view(np.uint32), base[gi].view(np.uint32)), gi
+    if kind == "integer":
+        assert np.array_equal(got.astype(np.float64), ref)
+    else:
+        tol = og.tolerance_mfma(mag, win) + 2.0 ** -24 * np.abs(ref)
+        err = np.abs(got.astype(np.float64) - ref)
+        assert not (err > tol).any(), (int((err > tol).sum()), float((err / tol).max()))
+
+
 def test_single_group_is_dense():
     rng = np.random.default_rng(5)
     t, n, k = 384, 512, 1024

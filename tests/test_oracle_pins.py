@@ -348,6 +348,32 @@ def test_wgrad_exact_rational():
                 assert out[g, n, k] == float(acc), (g, n, k)
 
 
+def test_wgrad_accumulate_exact_rational():
+    """main_grad + dY_g^T X_g against exact rational sums (the fp32 base
+    value plus the exact product, rounded once); an expert without rows
+    keeps its slice bit for bit, negative zeros included."""
+    rng = np.random.default_rng(24)
+    N, K, splits = 3, 4, [128, 0, 128]
+    T = sum(splits)
+    dycq, dycs = _rand_mx(rng, N, T)
+    xcq, xcs = _rand_mx(rng, K, T)
+    base = rng.standard_normal((3, N, K)).astype(np.float32)
+    base[1, 0, :] = -0.0
+    out = ogemm.wgrad_accumulate(base, dycq, dycs, xcq, xcs, splits)
+    assert np.array_equal(out[1].astype(np.float32).view(np.uint32), base[1].view(np.uint32))
+    for g, (r0, r1) in [(0, (0, 128)), (2, (128, 256))]:
+        for n in range(N):
+            for k in range(K):
+                acc = Fraction(float(base[g, n, k])) + sum(
+                    _exact(dycq[n, t], dycs[n, t // 32]) * _exact(xcq[k, t], xcs[k, t // 32])
+                    for t in range(r0, r1))
+                assert out[g, n, k] == float(acc), (g, n, k)
+    # a zero base gives the plain wgrad
+    zero = np.zeros((3, N, K), dtype=np.float32)
+    assert np.array_equal(ogemm.wgrad_accumulate(zero, dycq, dycs, xcq, xcs, splits),
+                          ogemm.wgrad(dycq, dycs, xcq, xcs, splits))
+
+
 def test_grouped_equals_per_group_and_dense():
     rng = np.random.default_rng(23)
     G, N, K, splits = 4, 64, 128, [256, 0, 128, 128]

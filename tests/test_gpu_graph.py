@@ -1,0 +1,114 @@
+"""Graph capture and replay of the whole hot-path step with caller-owned
+outputs reused in place.  The pages ask for outputs written into caller
+buffers so that CUDA-graph replays reuse them ("Improve device-init grouped
+linear module with single grouped weight support", review thread on the
+`output=` argument), and the pages' tests replay captured graphs; here the
+eight launches of one step (quantize X and W, forward, requant X, quantize
+dY, dgrad, requant dY with dbias, wgrad) are captured once and replayed on
+fresh inputs copied into the captured input buffers.  Every kernel reduces
+in a fixed order, so each replay must equal, byte for byte, an eager run of
+the same inputs into separate buffers.  Eager work and synchronisations run
+between the replays."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import workloads as wl
+
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+class _Step:
+    """Input and output buffers of one step, and the step itself."""
+
+    def __init__(self, w, x, wt, dy):
+        g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+        u8 = dict(dtype=torch.uint8, device="cuda")
+        self.shape = (g, t, k, n)
+        self.ms = torch.from_numpy(w.m_splits).to("cuda")
+        self.x, self.wt, self.dy = x.to("cuda"), wt.to("cuda"), dy.to("cuda")
+        self.xo = mx.MXFP8Tensor(torch.empty(t, k, **u8), torch.empty(t, k // 32, **u8))
+        self.wo = mx.MXFP8Tensor(torch.empty(g * n, k, **u8), torch.empty(g * n, k // 32, **u8),
+                                 torch.empty(k, g * n, **u8), torch.empty(k, g * n // 32, **u8))
+        self.xc = mx.MXFP8Tensor(col_data=torch.empty(k, t, **u8),
+                                 col_scale=torch.empty(k, t // 32, **u8))
+        self.dyo = mx.MXFP8Tensor(torch.empty(t, n, **u8), torch.empty(t, n // 32, **u8))
+        self.dyc = mx.MXFP8Tensor(col_data=torch.empty(n, t, **u8),
+                                  col_scale=torch.empty(n, t // 32, **u8))
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.y = torch.empty(t, n, **f32)
+        self.dx = torch.empty(t, k, **f32)
+        self.dw = torch.empty(g, n, k, **f32)
+        self.db = torch.empty(g, n, **f32)
+        self.ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8)
+
+    def run(self):
+        g, t, k, n = self.shape
+        ms = self.ms
+        mx.group_quantize(self.x, mx.ROWWISE, out=self.xo)
+        mx.group_quantize(self.wt, mx.ROWWISE | mx.COLWISE, out=self.wo)
+        mx.grouped_gemm("NT", self.xo.row_data, self.xo.row_scale, self.wo.row_data,
+                        self.wo.row_scale, ms, t, n, k, torch.float32, self.y)
+        mx.requant_colwise(self.xo.row_data, self.xo.row_scale, out=self.xc)
+        mx.group_quantize(self.dy, mx.ROWWISE, out=self.dyo)
+        mx.grouped_gemm("NN", self.dyo.row_data, self.dyo.row_scale, self.wo.col_data,
+                        self.wo.col_scale, ms, t, n, k, torch.float32, self.dx)
+        mx.requant_colwise(self.dyo.row_data, self.dyo.row_scale, ms, with_dbias=True,
+                           out=self.dyc, dbias=self.db, workspace=self.ws)
+        mx.grouped_gemm("TN", self.dyc.col_data, self.dyc.col_scale, self.xc.col_data,
+                        self.xc.col_scale, ms, t, n, k, torch.float32, self.dw)
+
+    def outputs(self):
+        return {"x_row": self.xo.row_data, "x_row_scale": self.xo.row_scale,
+                "w_row": self.wo.row_data, "w_col": self.wo.col_data,
+                "w_col_scale": self.wo.col_scale, "x_col": self.xc.col_data,
+                "x_col_scale": self.xc.col_scale, "dy_row": self.dyo.row_data,
+                "dy_col": self.dyc.col_data, "dy_col_scale": self.dyc.col_scale,
+                "y": self.y, "dx": self.dx, "dw": self.dw, "dbias": self.db}
+
+
+def _inputs(w, i):
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    x = wl.bf16_normal([w.wid, wl.STREAM_X, 200 + i], (t, k))
+    wt = wl.bf16_normal([w.wid, wl.STREAM_W, 200 + i], (g * n, k), std=0.02).reshape(g, n, k)
+    dy = wl.bf16_normal([w.wid, wl.STREAM_DY, 200 + i], (t, n))
+    return x, wt, dy
+
+
+def test_graph_replay_matches_eager():
+    w = wl.make("small_moe8")
+    cap = _Step(w, *_inputs(w, 0))
+    log("graph: warm-up on a side stream")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cap.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("graph: capture")
+    with torch.cuda.graph(graph):
+        cap.run()
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        x, wt, dy = _inputs(w, i)
+        cap.x.copy_(x.to("cuda"))
+        cap.wt.copy_(wt.to("cuda"))
+        cap.dy.copy_(dy.to("cuda"))
+        log(f"graph: replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in cap.outputs().items()}
+        log(f"graph: eager run {i}")
+        ref = _Step(w, x, wt, dy)
+        ref.run()
+        torch.cuda.synchronize()
+        for name, want in ref.outputs().items():
+            a = got[name].view(torch.uint8) if got[name].dtype == torch.float32 else got[name]
+            b = want.view(torch.uint8) if want.dtype == torch.float32 else want
+            assert torch.equal(a, b), f"replay {i}: {name} differs from the eager run"
+        del ref

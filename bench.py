@@ -249,6 +249,33 @@ def main():
         torch.cuda.synchronize()
         acc_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
         del main_grad
+
+    # Outside the step: gradients of a routing-scaled bias (dbias weighted by
+    # each token's scale, and each token's scale gradient) from row-wise dY.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    r_scales = torch.rand(t, device=dev, generator=gen)
+    r_bias = torch.randn(g, n, device=dev, generator=gen)
+    sb_ws = torch.empty(mx.load_library().mxfp8_scaled_bias_workspace_bytes(t, n), **u8)
+    sb = lambda: mx.grouped_scaled_bias_grad(  # noqa: E731
+        dyo.row_data, dyo.row_scale, ms, r_scales, r_bias, workspace=sb_ws)
+    for _ in range(2):
+        sb()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(max(args.steps, 3)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        sb()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    sb_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    # dY codes and scales read once, scales and bias read, both partial sums
+    # written and read back, both outputs written
+    sb_bytes = (t * n * (1 + 1 / 32) + t * 4 + g * n * 4 + 2 * (t // 128) * n * 4
+                + 2 * t * (n // 512) * 4 + g * n * 4 + t * 4)
     flop_one = 2.0 * t * n * k
     gemm_ms = per["gemm_fprop"] + per["gemm_dgrad"] + per["gemm_wgrad"]
     gemm_tflops = 3 * flop_one / (gemm_ms * 1e-3) / 1e12
@@ -287,6 +314,10 @@ def main():
         "wgrad_accumulate": None if acc_ms is None else {
             "ms": round(acc_ms, 4), "tflops": round(flop_one / (acc_ms * 1e-3) / 1e12, 2),
             "note": "main_grad += dY^T X in fp32, outside the step"},
+        "scaled_bias_grad": {"ms": round(sb_ms, 4),
+                             "gbs": round(sb_bytes / (sb_ms * 1e-3) / 1e9, 1),
+                             "note": "dbias and dscales of a routing-scaled bias from row-wise "
+                                     "dY, outside the step"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),

@@ -149,6 +149,31 @@ mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mxfp8_grouped_scaled_bias_grad -- gradients of a bias scaled by each
+ * token's routing scale, from row-wise MXFP8 dY ([P3244] Greptile Summary:
+ * scaled-bias gradient reductions; its flowchart takes the bias and
+ * routing-scale reductions from the dequantized gradient).  With the forward
+ * out_r = x_r W_g^T + s_r b_g for row r of expert g:
+ *   dbias[g, n] = sum over rows r of expert g of s_r * dY[r, n]
+ *   dscales[r]  = sum over n of dY[r, n] * b[g, n]
+ * dY is dequantized exactly; sums in fp32 in a fixed order (bitwise
+ * reproducible).  An expert with no rows gets dbias[g] = 0.
+ *   q_row [T, N] + s_row [T, N/32]: row-wise dY; m_splits: device int64 [G];
+ *   scales: device fp32 [T] (needed for dbias); bias: device fp32 [G, N]
+ *   (needed for dscales); dbias: fp32 [G, N] or NULL; dscales: fp32 [T] or
+ *   NULL (at least one); workspace: device, at least
+ *   mxfp8_scaled_bias_workspace_bytes(T, N) bytes.
+ * Errors: EINVAL for NULL inputs, neither output requested, an output without
+ * its input, T % 128, N % 512, host m_splits, a small workspace.
+ */
+size_t mxfp8_scaled_bias_workspace_bytes(int64_t T, int64_t N);
+mxfp8_status mxfp8_grouped_scaled_bias_grad(const uint8_t* q_row, const uint8_t* s_row,
+                                            int64_t T, int64_t N, const int64_t* m_splits,
+                                            int32_t G, const float* scales, const float* bias,
+                                            float* dbias, float* dscales, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * mxfp8_grouped_gemm -- the three grouped GEMMs of an expert linear
  * y = x W^T (in_features K, out_features N, grouped weight [G, N, K],
  * [P3224] Greptile Summary) on MXFP8 operands, fp32 accumulation.

@@ -177,6 +177,35 @@ def grouped_dbias(row_data, row_scale, m_splits, dbias=None, workspace=None, str
     return dbias
 
 
+def grouped_scaled_bias_grad(row_data, row_scale, m_splits, scales=None, bias=None,
+                             want_dbias=True, want_dscales=True, workspace=None, stream=None):
+    """Gradients of a routing-scaled bias from row-wise MXFP8 dY [T, N]:
+    dbias [G, N] = sum over each expert's rows of scales[r] dY[r] (needs
+    scales [T] fp32) and dscales [T] = dY[r] . bias[g] (needs bias [G, N]
+    fp32).  Returns (dbias or None, dscales or None)."""
+    lib = _lib()
+    t, n = row_data.shape
+    _need(row_data, torch.uint8, (t, n), "row_data")
+    _need(row_scale, torch.uint8, (t, n // 32), "row_scale")
+    ms = _splits(m_splits)
+    g = ms.numel()
+    dbias = _empty((g, n), torch.float32, row_data) if want_dbias else None
+    dscales = _empty((t,), torch.float32, row_data) if want_dscales else None
+    if want_dbias:
+        _need(scales, torch.float32, (t,), "scales")
+    if want_dscales:
+        _need(bias, torch.float32, (g, n), "bias")
+    need = lib.mxfp8_scaled_bias_workspace_bytes(t, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=row_data.device)
+    st = lib.mxfp8_grouped_scaled_bias_grad(
+        _ptr(row_data), _ptr(row_scale), t, n, _ptr(ms), g, _ptr(scales) if want_dbias else None,
+        _ptr(bias) if want_dscales else None, _ptr(dbias), _ptr(dscales), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _native.check(st, "mxfp8_grouped_scaled_bias_grad")
+    return dbias, dscales
+
+
 def grouped_gemm(layout, a_data, a_scale, b_data, b_scale, m_splits, tokens, n, k,
                  out_dtype=torch.float32, out=None, stream=None):
     """One grouped GEMM of an expert linear (in_features k, out_features n).

@@ -142,6 +142,40 @@ mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int
   return hip_status(e, fn);
 }
 
+size_t mxfp8_scaled_bias_workspace_bytes(int64_t T, int64_t N) {
+  if (T <= 0 || N <= 0) return 0;
+  return mx::scaled_bias_workspace_bytes(T, N);
+}
+
+mxfp8_status mxfp8_grouped_scaled_bias_grad(const uint8_t* q_row, const uint8_t* s_row,
+                                            int64_t T, int64_t N, const int64_t* m_splits,
+                                            int32_t G, const float* scales, const float* bias,
+                                            float* dbias, float* dscales, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const char* fn = "mxfp8_grouped_scaled_bias_grad";
+  REQUIRE(q_row && s_row, "%s: NULL data/scale pointer", fn);
+  REQUIRE(dbias || dscales, "%s: neither dbias nor dscales requested", fn);
+  REQUIRE(!dbias || scales, "%s: dbias needs the routing scales", fn);
+  REQUIRE(!dscales || bias, "%s: dscales needs the bias", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
+          (long long)N);
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  if (T == 0) {
+    // no rows: dbias is zero for every expert, dscales is empty
+    if (dbias != nullptr)
+      return hip_status(mx::launch_dbias_finalize(nullptr, m_splits, G, 0, N, dbias,
+                                                  as_stream(stream)), fn);
+    return ok();
+  }
+  REQUIRE(workspace != nullptr && workspace_bytes >= mx::scaled_bias_workspace_bytes(T, N),
+          "%s: needs a workspace of %zu bytes", fn, mx::scaled_bias_workspace_bytes(T, N));
+  return hip_status(mx::launch_scaled_bias_grad(q_row, s_row, T, N, m_splits, G, scales, bias,
+                                                dbias, dscales, workspace, as_stream(stream)),
+                    fn);
+}
+
 mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
                                 const uint8_t* b_data, const uint8_t* b_scale, void* c,
                                 int32_t c_dtype, int64_t T, int64_t N, int64_t K,

@@ -17,6 +17,11 @@ hipError_t launch_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, in
                                   hipStream_t st);
 hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int64_t T, int64_t N,
                                 float* partial, hipStream_t st);
+hipError_t launch_scaled_bias_grad(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                   int64_t N, const int64_t* m_splits, int32_t G,
+                                   const float* scales, const float* bias, float* dbias,
+                                   float* dscale, void* workspace, hipStream_t st);
+size_t scaled_bias_workspace_bytes(int64_t T, int64_t N);
 hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,
                                  int64_t T, int64_t K, float* dbias, hipStream_t st);
 hipError_t launch_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,

@@ -568,6 +568,173 @@ __global__ __launch_bounds__(256) void dbias_partial_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// scaled-bias and routing-scale gradients from row-wise data
+// ---------------------------------------------------------------------------
+//
+// With a bias scaled by each token's routing scale, out_r = x_r W_g^T +
+// s_r b_g, the gradients taken from the dequantized output gradient dY are
+//   dbias[g, n] = sum over rows r of expert g of s_r dY[r, n]
+//   dscale[r]   = sum over n of dY[r, n] b[g, n]
+// ("[Pytorch] Add support for row-wise quanted input for grouped gemm",
+// Greptile Summary: scaled-bias gradient reductions and the flowchart's
+// Dequantize -> bias and routing-scale reductions; the formulas are the
+// plain gradients of that scaled bias).
+
+// Expert of every 128-row tile (-1 for a tile no expert covers), from the
+// device splits: thread sums over its share of experts, a scan across the
+// workgroup, then each thread labels its experts' tiles.  One workgroup;
+// any number of experts.  Splits that break the contract are clipped to T.
+__global__ __launch_bounds__(256) void tile_expert_kernel(const int64_t* __restrict__ m_splits,
+                                                          int32_t G, int64_t T,
+                                                          int32_t* __restrict__ tile_expert) {
+  __shared__ int64_t pre[256];
+  const int tid = threadIdx.x;
+  const int per = (G + 255) / 256;
+  const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
+  const int64_t ntile = T / kTileT;
+  for (int64_t i = tid; i < ntile; i += 256) tile_expert[i] = -1;
+  int64_t sum = 0;
+  for (int g = g0; g < g1; ++g) sum += max(m_splits[g], (int64_t)0);
+  pre[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int64_t v = tid >= d ? pre[tid - d] : 0;
+    __syncthreads();
+    pre[tid] += v;
+    __syncthreads();
+  }
+  int64_t off = pre[tid] - sum;   // first row of expert g0
+  for (int g = g0; g < g1; ++g) {
+    const int64_t m = max(m_splits[g], (int64_t)0);
+    const int64_t t_lo = min(off, T) / kTileT, t_hi = min(off + m, T) / kTileT;
+    for (int64_t i = t_lo; i < t_hi; ++i) tile_expert[i] = g;
+    off += m;
+  }
+}
+
+// Per 128-row tile and 512 columns: lane -> 8 columns (one 8-byte load per
+// row), wave -> 32 rows.  dbias_partial[tile, n] = sum over the tile's rows
+// of s_r dY[r, n] (rows in order within a wave, then the four waves);
+// dscale_partial[r, c] = the dot product of row r with the bias over column
+// block c.  Per chunk of 8 rows each lane keeps its partial dot products; a
+// reduce-scatter butterfly over the 64 lanes (each exchange halves the rows
+// a lane keeps) and a sum over 8 lanes finish them in 10 exchanges instead
+// of 6 per row.  Codes are decoded by the hardware conversion
+// (scale bytes up to kMaxFastScaleByte) or, above, by integer arithmetic.
+// Either output may be absent.
+__global__ __launch_bounds__(256) void scaled_bias_partial_kernel(
+    const uint8_t* __restrict__ q_row, const uint8_t* __restrict__ s_row, int64_t T, int64_t N,
+    const float* __restrict__ scales, const float* __restrict__ bias,
+    const int32_t* __restrict__ tile_expert, float* __restrict__ dbias_partial,
+    float* __restrict__ dscale_partial) {
+  __shared__ float red[4][8][64];
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 512 + 8 * lane;
+  const int64_t t0 = (int64_t)blockIdx.y * kTileT + wave * 32;
+  const int64_t ns = N / 32, nb = N / 512;
+  const int g = tile_expert[blockIdx.y];
+  const bool want_db = dbias_partial != nullptr, want_ds = dscale_partial != nullptr;
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (want_ds && g >= 0) {
+    const float4 b0 = *reinterpret_cast<const float4*>(bias + (int64_t)g * N + n0);
+    const float4 b1 = *reinterpret_cast<const float4*>(bias + (int64_t)g * N + n0 + 4);
+    bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
+    bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // rows in chunks of kRows: only one chunk's partial dot products are live
+  constexpr int kRows = 8;   // 16 needs 210 registers and ran slower
+#pragma unroll 1
+  for (int rc = 0; rc < 32; rc += kRows) {
+    float pr[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t row = t0 + rc + r;
+      const u32x2 c = *reinterpret_cast<const u32x2*>(q_row + row * N + n0);
+      const uint32_t byte = s_row[row * ns + (n0 >> 5)];
+      float d[8];
+      if (byte <= kMaxFastScaleByte) {
+        const float sc = e8m0_operand(byte);
+        const f32x2_t v0 = cvt2_e4m3_f32(c.x, sc);
+        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, sc, true);
+        const f32x2_t v2 = cvt2_e4m3_f32(c.y, sc);
+        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, sc, true);
+        d[0] = v0.x; d[1] = v0.y; d[2] = v1.x; d[3] = v1.y;
+        d[4] = v2.x; d[5] = v2.y; d[6] = v3.x; d[7] = v3.y;
+      } else {
+        const int se = (int)byte - 127;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          d[i] = __builtin_amdgcn_ldexpf(
+              decode_e4m3(((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu), se);
+      }
+      if (want_db) {
+        const float sr = scales[row];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sr * d[i];
+      }
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p += d[i] * bv[i];
+      pr[r] = p;
+    }
+    if (want_ds) {
+      // reduce-scatter over the top log2(kRows) lane bits: at the exchange
+      // with lane ^ m a lane keeps the lower half of its current rows if
+      // (lane & m) == 0, else the upper half, and adds its partner's copy of
+      // those rows; then the lanes that share those bits sum their row
+      int cnt = kRows;
+#pragma unroll
+      for (int m = 32; m >= 64 / kRows; m >>= 1) {
+        const bool up = (lane & m) != 0;
+        cnt >>= 1;
+#pragma unroll
+        for (int i = 0; i < kRows / 2; ++i) {
+          if (i < cnt) {
+            const float send = up ? pr[i] : pr[i + cnt];
+            const float keep = up ? pr[i + cnt] : pr[i];
+            pr[i] = keep + __shfl_xor(send, m);
+          }
+        }
+      }
+      float tot = pr[0];
+#pragma unroll
+      for (int m = 32 / kRows; m >= 1; m >>= 1) tot += __shfl_xor(tot, m);
+      int row = 0;   // lane bit 5 selected half of the rows, bit 4 a quarter, ...
+#pragma unroll
+      for (int m = 32, w = kRows / 2; m >= 64 / kRows; m >>= 1, w >>= 1)
+        row += (lane & m) ? w : 0;
+      if ((lane & (64 / kRows - 1)) == 0) dscale_partial[(t0 + rc + row) * nb + blockIdx.x] = tot;
+    }
+  }
+  if (!want_db) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i] = (red[0][i][lane] + red[1][i][lane]) + (red[2][i][lane] + red[3][i][lane]);
+    float* dst = dbias_partial + (int64_t)blockIdx.y * N + n0;
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// dscale[r] = sum over the column blocks of dscale_partial[r, c], in order.
+__global__ __launch_bounds__(256) void dscale_finalize_kernel(const float* __restrict__ partial,
+                                                              int64_t T, int64_t nb,
+                                                              float* __restrict__ dscale) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= T) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < nb; ++c) s += partial[r * nb + c];
+  dscale[r] = s;
+}
+
 // dbias[g, k] = sum over the 128-row tiles of expert g of partial[tile, k],
 // in tile order.  grid = (G, ceil(K / 256)).
 __global__ __launch_bounds__(256) void dbias_finalize_kernel(
@@ -767,6 +934,43 @@ hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int6
   dim3 grid((unsigned)(N / 256), (unsigned)(T / kTileT));
   hipLaunchKernelGGL(dbias_partial_kernel, grid, dim3(256), 0, st, q_row, s_row, T, N, partial);
   return hipGetLastError();
+}
+
+hipError_t launch_scaled_bias_grad(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
+                                   int64_t N, const int64_t* m_splits, int32_t G,
+                                   const float* scales, const float* bias, float* dbias,
+                                   float* dscale, void* workspace, hipStream_t st) {
+  // workspace: tile experts (int32, padded to 256 B), dbias partials
+  // [T/128, N], dscale partials [T, N/512]
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tile_expert = reinterpret_cast<int32_t*>(ws);
+  const int64_t ntile = T / kTileT;
+  float* dbp = reinterpret_cast<float*>(ws + ((ntile * 4 + 255) / 256) * 256);
+  float* dsp = dbp + ntile * N;
+  hipLaunchKernelGGL(tile_expert_kernel, dim3(1), dim3(256), 0, st, m_splits, G, T, tile_expert);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scaled_bias_partial_kernel, dim3((unsigned)(N / 512), (unsigned)ntile),
+                     dim3(256), 0, st, q_row, s_row, T, N, scales, bias, tile_expert,
+                     dbias != nullptr ? dbp : nullptr, dscale != nullptr ? dsp : nullptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dbias != nullptr) {
+    e = launch_dbias_finalize(dbp, m_splits, G, T, N, dbias, st);
+    if (e != hipSuccess) return e;
+  }
+  if (dscale != nullptr) {
+    hipLaunchKernelGGL(dscale_finalize_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0,
+                       st, dsp, T, N / 512, dscale);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+size_t scaled_bias_workspace_bytes(int64_t T, int64_t N) {
+  const int64_t ntile = T / kTileT;
+  return (size_t)(((ntile * 4 + 255) / 256) * 256) + (size_t)ntile * N * 4 +
+         (size_t)T * (N / 512) * 4;
 }
 
 hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,

@@ -225,6 +225,36 @@ def grouped_dbias(q_row, s_row, m_splits):
     return out
 
 
+def grouped_scaled_bias_grad(q_row, s_row, m_splits, scales, bias):
+    """Gradients of a bias scaled by each row's routing scale.
+
+    Reading (the pages name "scaled-bias gradient reductions" and "bias and
+    routing-scale reductions" taken from the dequantized gradient, "[Pytorch]
+    Add support for row-wise quanted input for grouped gemm", Greptile Summary
+    and its flowchart, without formulas): the forward adds s_r * b_g to the
+    output row r of expert g, so with dY the dequantized output gradient
+        dbias[g, n] = sum over rows r of g of s_r * dY[r, n]
+        dscales[r]  = sum over n of dY[r, n] * b[g, n]
+    Returns float64 (dbias [G, N], dscales [T]); an empty group's dbias row is
+    zero.  scales: [T]; bias: [G, N] (both taken as given, float64).
+    """
+    xh = dequantize_rowwise(q_row, s_row)
+    t, n = xh.shape
+    m = check_splits(m_splits, t)
+    s = np.asarray(scales, dtype=np.float64)
+    b = np.asarray(bias, dtype=np.float64)
+    dbias = np.zeros((len(m), n), dtype=np.float64)
+    dscales = np.zeros(t, dtype=np.float64)
+    row = 0
+    for g, mg in enumerate(m):
+        if mg:
+            rows = slice(row, row + mg)
+            dbias[g] = (s[rows, None] * xh[rows]).sum(axis=0)
+            dscales[rows] = xh[rows] @ b[g]
+        row += mg
+    return dbias, dscales
+
+
 def scale_shape(total_tokens, cols):
     """Shape of the row-wise scale tensor: (round_up(T,128), round_up(K/32,4))."""
     def round_up(v, mult):

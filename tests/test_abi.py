@@ -116,6 +116,17 @@ def test_wgrad_accumulate_rejects(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 2000, None) == 1   # G > 1024
 
 
+def test_scaled_bias_grad_rejects(lib):
+    f = lib.mxfp8_grouped_scaled_bias_grad
+    big = 1 << 30
+    assert f(FAKE, FAKE, 128, 512, FAKE, 1, FAKE, FAKE, None, None, FAKE, big, None) == 1  # no output
+    assert f(FAKE, FAKE, 128, 512, FAKE, 1, None, FAKE, FAKE, None, FAKE, big, None) == 1  # no scales
+    assert f(FAKE, FAKE, 128, 512, FAKE, 1, FAKE, None, None, FAKE, FAKE, big, None) == 1  # no bias
+    assert f(FAKE, FAKE, 100, 512, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 1  # T % 128
+    assert lib.mxfp8_scaled_bias_workspace_bytes(16384, 14336) == (
+        512 + 128 * 14336 * 4 + 16384 * 28 * 4)
+
+
 def test_convert_sweep_sizes_and_rejects(lib):
     assert lib.mxfp8_convert_sweep_bytes(0) == 2 << 24
     assert lib.mxfp8_convert_sweep_bytes(1) == 1 << 24

@@ -201,6 +201,44 @@ def test_grouped_dbias(splits):
         row += m
 
 
+@pytest.mark.parametrize("splits,n", [([128, 0, 256, 128], 1024), ([0, 0, 384], 512),
+                                      ([256, 128, 128, 0, 0, 640], 1536)])
+def test_scaled_bias_grad(splits, n):
+    """dbias = sum of scales[r] dY[r] per expert and dscales = dY[r] . bias[g]
+    from row-wise dY; fp32 sums held to 1e-5 * (sum of |terms|) + 1e-6."""
+    log(f"scaled bias grad {splits} n {n}")
+    rng = np.random.default_rng(sum(splits) + n)
+    t = sum(splits)
+    q, s = random_mx(rng, t, n)
+    scales = rng.random(t).astype(np.float32)
+    bias = rng.standard_normal((len(splits), n)).astype(np.float32)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    db, ds = mx.grouped_scaled_bias_grad(dev(q), dev(s), ms, dev(scales), dev(bias))
+    torch.cuda.synchronize()
+    ref_db, ref_ds = om.grouped_scaled_bias_grad(q, s, splits, scales, bias)
+    xh = np.abs(om.dequantize_rowwise(q, s))
+    mag_db = np.zeros_like(ref_db)
+    mag_ds = np.zeros_like(ref_ds)
+    row = 0
+    for g, m in enumerate(splits):
+        mag_db[g] = (scales[row:row + m, None].astype(np.float64) * xh[row:row + m]).sum(axis=0)
+        mag_ds[row:row + m] = xh[row:row + m] @ np.abs(bias[g].astype(np.float64))
+        row += m
+    assert np.all(np.abs(f64(db) - ref_db) <= og.tolerance_f32(mag_db))
+    assert np.all(np.abs(f64(ds) - ref_ds) <= og.tolerance_f32(mag_ds))
+    for g, m in enumerate(splits):
+        if m == 0:
+            assert np.all(f64(db)[g] == 0)
+    # either output alone
+    db2, none = mx.grouped_scaled_bias_grad(dev(q), dev(s), ms, dev(scales), None,
+                                            want_dscales=False)
+    none2, ds2 = mx.grouped_scaled_bias_grad(dev(q), dev(s), ms, None, dev(bias),
+                                             want_dbias=False)
+    torch.cuda.synchronize()
+    assert none is None and none2 is None
+    assert torch.equal(db2, db) and torch.equal(ds2, ds)
+
+
 def test_validate_splits():
     log("validate splits")
     cases = [([128, 256, 0], 384, 0), ([128, 100], 228, 2), ([-128, 256], 128, 1),

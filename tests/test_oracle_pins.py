@@ -281,6 +281,42 @@ def test_requant_can_clip():
     assert qc[0, 0] == 0x7E
 
 
+def test_scaled_bias_grad_special_cases_and_bruteforce():
+    """Unit scales give the ordinary grouped dbias; a zero bias gives zero
+    dscales; both outputs are linear in the scales / the bias; and a tiny
+    case is checked element by element with Python loops."""
+    rng = np.random.default_rng(31)
+    splits = [128, 0, 256]
+    t, n = sum(splits), 64
+    q = rng.integers(0, 256, size=(t, n)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x7E
+    s = rng.integers(120, 134, size=(t, n // 32)).astype(np.uint8)
+    ones = np.ones(t)
+    bias = rng.standard_normal((3, n))
+    db1, _ = om.grouped_scaled_bias_grad(q, s, splits, ones, bias)
+    assert np.allclose(db1, om.grouped_dbias(q, s, splits), rtol=1e-12, atol=0)
+    _, ds0 = om.grouped_scaled_bias_grad(q, s, splits, ones, np.zeros((3, n)))
+    assert np.all(ds0 == 0)
+    sc = rng.random(t)
+    db_a, ds_a = om.grouped_scaled_bias_grad(q, s, splits, sc, bias)
+    db_b, ds_b = om.grouped_scaled_bias_grad(q, s, splits, 2 * sc, 3 * bias)
+    assert np.allclose(db_b, 2 * db_a, rtol=1e-12) and np.allclose(ds_b, 3 * ds_a, rtol=1e-12)
+    assert np.all(db_a[1] == 0)
+    xh = om.dequantize_rowwise(q, s)
+    group_of = [0] * 128 + [2] * 256
+    for r in range(0, t, 29):
+        want = 0.0
+        for c in range(n):
+            want += float(xh[r, c]) * float(bias[group_of[r], c])
+        assert abs(ds_a[r] - want) <= 1e-9 * (abs(want) + 1)
+    for g, (r0, r1) in [(0, (0, 128)), (2, (128, 384))]:
+        for c in range(0, n, 7):
+            want = 0.0
+            for r in range(r0, r1):
+                want += float(sc[r]) * float(xh[r, c])
+            assert abs(db_a[g, c] - want) <= 1e-9 * (abs(want) + 1)
+
+
 # ----------------------------------------------------------------------------
 # grouped GEMM
 # ----------------------------------------------------------------------------

@@ -144,6 +144,26 @@ def cpu_baseline(w, budget_rows=4096, n_cols=2048):
                       f"{dt:.2f} s wall, float64 NumPy"}
 
 
+def _time_outside(fn, steps):
+    """Mean time (ms) of `fn` over max(steps, 3) launches after two warmups."""
+    import numpy as np
+    import torch
+
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(max(steps, 3)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -235,19 +255,7 @@ def main():
         main_grad = torch.zeros(g, n, k, dtype=torch.float32, device=dev)
         acc = lambda: mx.grouped_gemm_wgrad_accumulate(  # noqa: E731
             dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, main_grad)
-        for _ in range(2):
-            acc()
-        torch.cuda.synchronize()
-        pairs = []
-        for _ in range(max(args.steps, 3)):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            acc()
-            b.record()
-            pairs.append((a, b))
-        torch.cuda.synchronize()
-        acc_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+        acc_ms = _time_outside(acc, args.steps)
         del main_grad
 
     # Outside the step: gradients of a routing-scaled bias (dbias weighted by
@@ -257,25 +265,29 @@ def main():
     r_scales = torch.rand(t, device=dev, generator=gen)
     r_bias = torch.randn(g, n, device=dev, generator=gen)
     sb_ws = torch.empty(mx.load_library().mxfp8_scaled_bias_workspace_bytes(t, n), **u8)
-    sb = lambda: mx.grouped_scaled_bias_grad(  # noqa: E731
-        dyo.row_data, dyo.row_scale, ms, r_scales, r_bias, workspace=sb_ws)
-    for _ in range(2):
-        sb()
-    torch.cuda.synchronize()
-    pairs = []
-    for _ in range(max(args.steps, 3)):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        sb()
-        b.record()
-        pairs.append((a, b))
-    torch.cuda.synchronize()
-    sb_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    sb_ms = _time_outside(lambda: mx.grouped_scaled_bias_grad(
+        dyo.row_data, dyo.row_scale, ms, r_scales, r_bias, workspace=sb_ws), args.steps)
     # dY codes and scales read once, scales and bias read, both partial sums
     # written and read back, both outputs written
     sb_bytes = (t * n * (1 + 1 / 32) + t * 4 + g * n * 4 + 2 * (t // 128) * n * 4
                 + 2 * t * (n // 512) * 4 + g * n * 4 + t * 4)
+    # Outside the step: the fused expert MLP's activation (SwiGLU of the FC1
+    # output, quantized row- and column-wise for FC2) at the Nemotron-proxy
+    # MLP shape (T = 83968 tokens, FC1 out 2F = 2048), fused in one kernel and
+    # as the two-kernel chain it replaces.
+    sw_t, sw_f = 83968, 1024
+    hgen = torch.Generator(device=dev)
+    hgen.manual_seed(11)
+    h_sw = (torch.randn(sw_t, 2 * sw_f, device=dev, generator=hgen) * 3).to(torch.bfloat16)
+    sw_out = mx.swiglu_quantize(h_sw)
+    a_sw = mx.swiglu_fwd(h_sw)
+    sw_ms = _time_outside(lambda: mx.swiglu_quantize(h_sw, out=sw_out), args.steps)
+    sw_chain_ms = _time_outside(lambda: mx.group_quantize(
+        mx.swiglu_fwd(h_sw, out=a_sw), mx.ROWWISE | mx.COLWISE, out=sw_out), args.steps)
+    # fused: h read (4 B per output element), row + column copies written
+    sw_bytes = sw_t * sw_f * (4 + 2 * (1 + 1 / 32))
+    del h_sw, sw_out, a_sw
+
     flop_one = 2.0 * t * n * k
     gemm_ms = per["gemm_fprop"] + per["gemm_dgrad"] + per["gemm_wgrad"]
     gemm_tflops = 3 * flop_one / (gemm_ms * 1e-3) / 1e12
@@ -318,6 +330,11 @@ def main():
                              "gbs": round(sb_bytes / (sb_ms * 1e-3) / 1e9, 1),
                              "note": "dbias and dscales of a routing-scaled bias from row-wise "
                                      "dY, outside the step"},
+        "swiglu_quantize": {"ms": round(sw_ms, 4),
+                            "gbs": round(sw_bytes / (sw_ms * 1e-3) / 1e9, 1),
+                            "unfused_ms": round(sw_chain_ms, 4),
+                            "note": f"SwiGLU + row/col MXFP8 of h [{sw_t}, {2 * sw_f}] in one "
+                                    "kernel vs swiglu_fwd + group_quantize, outside the step"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),

@@ -249,6 +249,27 @@ mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t*
                               void* stream);
 
 /*
+ * mxfp8_swiglu_quantize -- SwiGLU fused with the MXFP8 quantize of its output,
+ * the FC2 input of the fused expert MLP ([P3545] Description: FC1 ->
+ * activation -> FC2 as one op; its saved-state commit: the FC2 wgrad reads
+ * the column-wise tiles of that input, the FC2 forward the row-wise ones).
+ * The bf16 activation a = silu(h[:, :F]) * h[:, F:] is formed in registers
+ * (exactly the bf16 values mxfp8_swiglu_fwd writes) and quantized as
+ * mxfp8_group_quantize quantizes a [T, F] tensor, without writing a:
+ * the outputs are byte-identical to mxfp8_swiglu_fwd followed by
+ * mxfp8_group_quantize.
+ *
+ *   h      [T, 2F] bf16 (device)
+ *   usage  MXFP8_ROWWISE | MXFP8_COLWISE (at least one)
+ *   q_row  [T, F] u8,  s_row [T, F/32] u8        (required iff ROWWISE)
+ *   q_col  [F, T] u8,  s_col [F, T/32] u8        (required iff COLWISE)
+ * Errors: EINVAL for NULL required pointers, T % 128, F % 512, usage == 0.
+ */
+mxfp8_status mxfp8_swiglu_quantize(const uint16_t* h, int64_t T, int64_t F, uint32_t usage,
+                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                   uint8_t* s_col, void* stream);
+
+/*
  * Backward of mxfp8_swiglu_fwd: given h [T, 2F] and da [T, F] (bf16), writes
  * dh [T, 2F] bf16: d gate = da * up * s * (1 + gate * (1 - s)), s = sigmoid(gate);
  * d up = da * silu(gate).  Errors as mxfp8_swiglu_fwd.

@@ -84,6 +84,31 @@ def _splits(m_splits, name="m_splits"):
     return m_splits
 
 
+def _mx_outputs(out, usage, t, k, like):
+    """Allocate (or check) the requested row-/column-wise buffers of a [t, k] tensor."""
+    out = out or MXFP8Tensor()
+    if usage & ROWWISE:
+        if out.row_data is None:
+            out.row_data = _empty((t, k), torch.uint8, like)
+            out.row_scale = _empty((t, k // 32), torch.uint8, like)
+        _need(out.row_data, torch.uint8, (t, k), "row_data")
+        _need(out.row_scale, torch.uint8, (t, k // 32), "row_scale")
+    if usage & COLWISE:
+        if out.col_data is None:
+            out.col_data = _empty((k, t), torch.uint8, like)
+            out.col_scale = _empty((k, t // 32), torch.uint8, like)
+        _need(out.col_data, torch.uint8, (k, t), "col_data")
+        _need(out.col_scale, torch.uint8, (k, t // 32), "col_scale")
+    return out
+
+
+def _mx_ptrs(out, usage):
+    row = usage & ROWWISE
+    col = usage & COLWISE
+    return (_ptr(out.row_data) if row else None, _ptr(out.row_scale) if row else None,
+            _ptr(out.col_data) if col else None, _ptr(out.col_scale) if col else None)
+
+
 def group_quantize(x, usage=ROWWISE, out: Optional[MXFP8Tensor] = None, stream=None):
     """bf16 [T, K] (or [G, N, K], taken as [G*N, K]) -> MXFP8Tensor."""
     lib = _lib()
@@ -91,26 +116,23 @@ def group_quantize(x, usage=ROWWISE, out: Optional[MXFP8Tensor] = None, stream=N
         x = x.reshape(-1, x.shape[-1])
     t, k = x.shape
     _need(x, torch.bfloat16, (t, k), "x")
-    out = out or MXFP8Tensor()
-    if usage & ROWWISE:
-        if out.row_data is None:
-            out.row_data = _empty((t, k), torch.uint8, x)
-            out.row_scale = _empty((t, k // 32), torch.uint8, x)
-        _need(out.row_data, torch.uint8, (t, k), "row_data")
-        _need(out.row_scale, torch.uint8, (t, k // 32), "row_scale")
-    if usage & COLWISE:
-        if out.col_data is None:
-            out.col_data = _empty((k, t), torch.uint8, x)
-            out.col_scale = _empty((k, t // 32), torch.uint8, x)
-        _need(out.col_data, torch.uint8, (k, t), "col_data")
-        _need(out.col_scale, torch.uint8, (k, t // 32), "col_scale")
-    row = usage & ROWWISE
-    col = usage & COLWISE
-    st = lib.mxfp8_group_quantize(
-        _ptr(x), t, k, usage, _ptr(out.row_data) if row else None,
-        _ptr(out.row_scale) if row else None, _ptr(out.col_data) if col else None,
-        _ptr(out.col_scale) if col else None, _stream(stream))
+    out = _mx_outputs(out, usage, t, k, x)
+    st = lib.mxfp8_group_quantize(_ptr(x), t, k, usage, *_mx_ptrs(out, usage), _stream(stream))
     _native.check(st, "mxfp8_group_quantize")
+    return out
+
+
+def swiglu_quantize(h, usage=ROWWISE | COLWISE, out: Optional[MXFP8Tensor] = None,
+                    stream=None):
+    """h [T, 2F] bf16 -> MXFP8Tensor of a = silu(h[:, :F]) * h[:, F:] (bf16
+    rounded, as swiglu_fwd gives it) without writing a."""
+    lib = _lib()
+    t, f2 = h.shape
+    f = f2 // 2
+    _need(h, torch.bfloat16, (t, 2 * f), "h")
+    out = _mx_outputs(out, usage, t, f, h)
+    st = lib.mxfp8_swiglu_quantize(_ptr(h), t, f, usage, *_mx_ptrs(out, usage), _stream(stream))
+    _native.check(st, "mxfp8_swiglu_quantize")
     return out
 
 

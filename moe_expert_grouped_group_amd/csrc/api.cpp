@@ -244,6 +244,26 @@ mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t*
   return hip_status(mx::launch_swiglu_fwd(h, T, F, a, as_stream(stream)), fn);
 }
 
+mxfp8_status mxfp8_swiglu_quantize(const uint16_t* h, int64_t T, int64_t F, uint32_t usage,
+                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                   uint8_t* s_col, void* stream) {
+  const char* fn = "mxfp8_swiglu_quantize";
+  REQUIRE(h != nullptr, "%s: h is NULL", fn);
+  REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
+          "%s: usage must be a non-empty combination of MXFP8_ROWWISE and MXFP8_COLWISE", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(F > 0 && F % 512 == 0, "%s: F = %lld must be a positive multiple of 512", fn,
+          (long long)F);
+  const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
+  REQUIRE(!row || (q_row && s_row), "%s: ROWWISE requested but q_row/s_row is NULL", fn);
+  REQUIRE(!col || (q_col && s_col), "%s: COLWISE requested but q_col/s_col is NULL", fn);
+  if (T == 0) return ok();
+  return hip_status(mx::launch_swiglu_quant(h, T, F, row ? q_row : nullptr, row ? s_row : nullptr,
+                                            col ? q_col : nullptr, col ? s_col : nullptr,
+                                            as_stream(stream)),
+                    fn);
+}
+
 mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                               uint16_t* dh, void* stream) {
   const char* fn = "mxfp8_swiglu_bwd";

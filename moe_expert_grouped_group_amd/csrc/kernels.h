@@ -28,6 +28,8 @@ hipError_t launch_validate_splits(const int64_t* m_splits, int32_t G, int64_t T,
                                   hipStream_t st);
 hipError_t launch_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,
                              hipStream_t st);
+hipError_t launch_swiglu_quant(const uint16_t* h, int64_t T, int64_t F, uint8_t* q_row,
+                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st);
 hipError_t launch_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                              uint16_t* dh, hipStream_t st);
 size_t convert_sweep_bytes(int32_t mode);   // 0 for an unknown mode

@@ -243,6 +243,54 @@ __device__ __forceinline__ void load_bf16_tile(const uint16_t* __restrict__ x, i
         reinterpret_cast<const u32x4*>(x + (t0 * K + k0 + 16 * j * K) + off));
 }
 
+// Column-wise quantize of a staged 128 x 128 bf16 tile (columns k0.., tokens
+// t0..): thread -> column quad q = tid / 8, 16-token chunk j = tid % 8.
+__device__ __forceinline__ void colwise_pass_bf16(const uint8_t* lds, int64_t T, int64_t K,
+                                                  int64_t k0, int64_t t0,
+                                                  uint8_t* __restrict__ q_col,
+                                                  uint8_t* __restrict__ s_col) {
+  const int j = threadIdx.x & 7, q = threadIdx.x >> 3;
+  // row r of the chunk as bf16 pairs, columns (0, 1) and (2, 3)
+  uint32_t lo[16], hi[16];
+  const uint8_t* src = lds + opaque_off(lds_off_bf16(16 * j, 8 * q));   // row 16j + r at r * 256
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src + r * 256);
+    lo[r] = v.x;
+    hi[r] = v.y;
+  }
+  uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    mlo = max_u16x2(mlo, lo[r] & 0x7FFF7FFFu);
+    mhi = max_u16x2(mhi, hi[r] & 0x7FFF7FFFu);
+  }
+  mlo = max_u16x2(mlo, lane_xor1(mlo));   // the block's other 16 tokens
+  mhi = max_u16x2(mhi, lane_xor1(mhi));
+  const uint32_t xb[4] = {scale_byte_from_exp((mlo & 0xFFFFu) >> 7),
+                          scale_byte_from_exp((mlo >> 16) >> 7),
+                          scale_byte_from_exp((mhi & 0xFFFFu) >> 7),
+                          scale_byte_from_exp((mhi >> 16) >> 7)};
+  const float sc[4] = {e8m0_operand(xb[0]), e8m0_operand(xb[1]), e8m0_operand(xb[2]),
+                       e8m0_operand(xb[3])};
+  // a byte permute gathers the same column of two rows into one bf16 pair
+  uint32_t o[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int r = 4 * g;
+    o[0][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(lo[r + 1], lo[r], 0x05040100u),
+                             __builtin_amdgcn_perm(lo[r + 3], lo[r + 2], 0x05040100u), sc[0]);
+    o[1][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(lo[r + 1], lo[r], 0x07060302u),
+                             __builtin_amdgcn_perm(lo[r + 3], lo[r + 2], 0x07060302u), sc[1]);
+    o[2][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(hi[r + 1], hi[r], 0x05040100u),
+                             __builtin_amdgcn_perm(hi[r + 3], hi[r + 2], 0x05040100u), sc[2]);
+    o[3][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(hi[r + 1], hi[r], 0x07060302u),
+                             __builtin_amdgcn_perm(hi[r + 3], hi[r + 2], 0x07060302u), sc[3]);
+  }
+  float unused[4] = {0.f, 0.f, 0.f, 0.f};
+  colwise_store<false>(o, xb, unused, T, K, k0, t0, q_col, s_col, nullptr);
+}
+
 // Persistent: workgroup b takes tiles b, b + gridDim.x, ...; the loads of its
 // next tile are issued before the column-wise pass of the current one, so
 // each workgroup keeps a tile of reads in flight while it computes.
@@ -252,7 +300,6 @@ __global__ __launch_bounds__(kColThreads) void quant_rowcol_kernel(
     int32_t ntk, int32_t ntiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytesBf16];
   const int tid = threadIdx.x;
-  const int j = tid & 7, q = tid >> 3;
   int tile = blockIdx.x;
   u32x4 w[8];
   load_bf16_tile(x, K, tile, ntk, w);
@@ -284,45 +331,7 @@ __global__ __launch_bounds__(kColThreads) void quant_rowcol_kernel(
     const int next = tile + (int)gridDim.x;
     if (next < ntiles) load_bf16_tile(x, K, next, ntk, w);
 
-    // column-wise: row r of the chunk as bf16 pairs, columns (0, 1) and (2, 3)
-    uint32_t lo[16], hi[16];
-    const uint8_t* src = lds + opaque_off(lds_off_bf16(16 * j, 8 * q));   // row 16j + r at r * 256
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint2 v = *reinterpret_cast<const uint2*>(src + r * 256);
-      lo[r] = v.x;
-      hi[r] = v.y;
-    }
-    uint32_t mlo = 0, mhi = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      mlo = max_u16x2(mlo, lo[r] & 0x7FFF7FFFu);
-      mhi = max_u16x2(mhi, hi[r] & 0x7FFF7FFFu);
-    }
-    mlo = max_u16x2(mlo, lane_xor1(mlo));   // the block's other 16 tokens
-    mhi = max_u16x2(mhi, lane_xor1(mhi));
-    const uint32_t xb[4] = {scale_byte_from_exp((mlo & 0xFFFFu) >> 7),
-                            scale_byte_from_exp((mlo >> 16) >> 7),
-                            scale_byte_from_exp((mhi & 0xFFFFu) >> 7),
-                            scale_byte_from_exp((mhi >> 16) >> 7)};
-    const float sc[4] = {e8m0_operand(xb[0]), e8m0_operand(xb[1]), e8m0_operand(xb[2]),
-                         e8m0_operand(xb[3])};
-    // a byte permute gathers the same column of two rows into one bf16 pair
-    uint32_t o[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r = 4 * g;
-      o[0][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(lo[r + 1], lo[r], 0x05040100u),
-                               __builtin_amdgcn_perm(lo[r + 3], lo[r + 2], 0x05040100u), sc[0]);
-      o[1][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(lo[r + 1], lo[r], 0x07060302u),
-                               __builtin_amdgcn_perm(lo[r + 3], lo[r + 2], 0x07060302u), sc[1]);
-      o[2][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(hi[r + 1], hi[r], 0x05040100u),
-                               __builtin_amdgcn_perm(hi[r + 3], hi[r + 2], 0x05040100u), sc[2]);
-      o[3][g] = cvt4_bf16_e4m3(__builtin_amdgcn_perm(hi[r + 1], hi[r], 0x07060302u),
-                               __builtin_amdgcn_perm(hi[r + 3], hi[r + 2], 0x07060302u), sc[3]);
-    }
-    float unused[4] = {0.f, 0.f, 0.f, 0.f};
-    colwise_store<false>(o, xb, unused, T, K, k0, t0, q_col, s_col, nullptr);
+    colwise_pass_bf16(lds, T, K, k0, t0, q_col, s_col);
     if (next >= ntiles) break;
     __syncthreads();   // every column read of this tile is done before the next LDS write
     tile = next;
@@ -873,6 +882,60 @@ __global__ __launch_bounds__(256) void convert_sweep_kernel(int32_t mode, uint8_
 }
 
 // ---------------------------------------------------------------------------
+// SwiGLU fused with the MXFP8 quantize of its output
+// ---------------------------------------------------------------------------
+
+// a = silu(gate) * up of two bf16 pairs, as swiglu_fwd_kernel computes it
+// (fp32 math, round to nearest even to bf16), packed as a bf16 pair.
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
+  const float g0 = bf16_to_f32(gw & 0xFFFFu), g1 = bf16_to_f32(gw >> 16);
+  const float u0 = bf16_to_f32(uw & 0xFFFFu), u1 = bf16_to_f32(uw >> 16);
+  return f32_to_bf16(silu_f(g0) * u0) | (f32_to_bf16(silu_f(g1) * u1) << 16);
+}
+
+// h [T, 2F] bf16 (gate = columns [0, F), up = [F, 2F)) -> a = SwiGLU(h) [T, F]
+// quantized row-wise ([T, F] + [T, F/32]) and/or column-wise ([F, T] +
+// [F, T/32]) without writing a: the 128 x 128 tile of a is formed in
+// registers from the gate and up tiles, quantized row-wise from registers and
+// column-wise from LDS, exactly as quant_rowcol_kernel quantizes a bf16 tile.
+// The bytes equal swiglu_fwd_kernel followed by the group quantize.
+__global__ __launch_bounds__(kColThreads) void swiglu_quant_kernel(
+    const uint16_t* __restrict__ h, int64_t T, int64_t F, uint8_t* __restrict__ q_row,
+    uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytesBf16];
+  const int tid = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * kTileK;
+  const int64_t t0 = (int64_t)blockIdx.y * kTileT;
+  const int64_t ld = 2 * F;
+  const uint32_t off = (uint32_t)(tid >> 4) * (uint32_t)ld + (tid & 15) * 8;
+  const uint32_t ro = (uint32_t)(tid >> 4) * (uint32_t)F + (tid & 15) * 8;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int idx = tid + kColThreads * jj;
+    const int r = idx >> 4, cc = idx & 15;
+    const uint16_t* hb = h + (t0 + 16 * jj) * ld + k0;   // uniform
+    const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hb + off));
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hb + F + off));
+    const uint4 a = make_uint4(swiglu_pair(g.x, u.x), swiglu_pair(g.y, u.y),
+                               swiglu_pair(g.z, u.z), swiglu_pair(g.w, u.w));
+    if (q_col != nullptr)
+      *reinterpret_cast<u32x4*>(&lds[lds_off_bf16(r, cc * 16)]) = u32x4{a.x, a.y, a.z, a.w};
+    if (q_row != nullptr) {
+      // lanes 4b..4b+3 of a quad hold the 32 values of one block
+      const uint32_t amax = quad_max(chunk_amax_bits(a));
+      const uint32_t byte = scale_byte_from_exp(amax >> 7);
+      const int64_t rb = t0 * F + k0 + 16 * jj * F;   // uniform
+      *reinterpret_cast<uint2*>(q_row + rb + ro) = encode_chunk(a, byte);
+      const uint32_t bytes4 = gather_blocks4(byte);
+      if ((tid & 15) == 0) *reinterpret_cast<uint32_t*>(s_row + (rb >> 5) + (ro >> 5)) = bytes4;
+    }
+  }
+  if (q_col == nullptr) return;
+  __syncthreads();
+  colwise_pass_bf16(lds, T, F, k0, t0, q_col, s_col);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1011,6 +1074,14 @@ size_t convert_sweep_bytes(int32_t mode) {
 hipError_t launch_convert_sweep(int32_t mode, uint8_t* out, hipStream_t st) {
   const uint32_t n = mode == 2 ? 1u << 16 : 1u << 24;
   hipLaunchKernelGGL(convert_sweep_kernel, dim3(n / 256), dim3(256), 0, st, mode, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant(const uint16_t* h, int64_t T, int64_t F, uint8_t* q_row,
+                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st) {
+  dim3 grid((unsigned)(F / kTileK), (unsigned)(T / kTileT));
+  hipLaunchKernelGGL(swiglu_quant_kernel, grid, dim3(kColThreads), 0, st, h, T, F, q_row, s_row,
+                     q_col, s_col);
   return hipGetLastError();
 }
 

@@ -106,6 +106,14 @@ def test_swiglu_and_validate_reject(lib):
     assert lib.mxfp8_swiglu_fwd(FAKE, 4, 6, FAKE, None) == 1
     assert lib.mxfp8_swiglu_bwd(FAKE, None, 4, 8, FAKE, None) == 1
     assert lib.mxfp8_validate_splits(FAKE, 1, 128, None, None) == 1
+    q = lib.mxfp8_swiglu_quantize
+    assert q(None, 128, 512, 3, FAKE, FAKE, FAKE, FAKE, None) == 1        # no h
+    assert q(FAKE, 100, 512, 3, FAKE, FAKE, FAKE, FAKE, None) == 1        # T % 128
+    assert q(FAKE, 128, 500, 3, FAKE, FAKE, FAKE, FAKE, None) == 1        # F % 512
+    assert q(FAKE, 128, 512, 0, FAKE, FAKE, FAKE, FAKE, None) == 1        # usage 0
+    assert q(FAKE, 128, 512, 2, FAKE, FAKE, None, FAKE, None) == 1        # COLWISE, no q_col
+    assert q(FAKE, 128, 512, 1, None, FAKE, None, None, None) == 1        # ROWWISE, no q_row
+    assert q(FAKE, 0, 512, 3, FAKE, FAKE, FAKE, FAKE, None) == 0          # T == 0: nothing enqueued
 
 
 def test_wgrad_accumulate_rejects(lib):

@@ -259,3 +259,82 @@ def test_swiglu(t, f):
     torch.cuda.synchronize()
     assert og.within_bf16_ulp(f64(a), osw.swiglu_fwd(f64(h))).all()
     assert og.within_bf16_ulp(f64(dh), osw.swiglu_bwd(f64(h), f64(da))).all()
+
+
+def _swiglu_input(t, f, seed):
+    """FC1-output-like h [T, 2F] bf16: N(0, 3^2), with the gate of the first
+    32 rows zeroed (all-zero blocks, signed zeros from negative up values)."""
+    rng = np.random.default_rng(seed)
+    h = (rng.standard_normal((t, 2 * f)) * 3).astype(np.float32)
+    h[:32, :f] = 0.0
+    return torch.from_numpy(h).to(torch.bfloat16)
+
+
+def _mx_bytes(out):
+    return [u8(b) for b in (out.row_data, out.row_scale, out.col_data, out.col_scale)
+            if b is not None]
+
+
+@pytest.mark.parametrize("usage", [mx.ROWWISE | mx.COLWISE, mx.ROWWISE, mx.COLWISE])
+@pytest.mark.parametrize("t,f,seed", [(256, 1024, 11), (384, 512, 12), (1024, 1536, 13)])
+def test_swiglu_quantize_matches_unfused(usage, t, f, seed):
+    """The fused kernel gives the bytes of swiglu_fwd followed by the group
+    quantize (each pinned to the oracle by the tests above)."""
+    log(f"swiglu_quantize vs unfused usage {usage} {t}x{f}")
+    h = _swiglu_input(t, f, seed).to("cuda")
+    fused = mx.swiglu_quantize(h, usage)
+    unfused = mx.group_quantize(mx.swiglu_fwd(h), usage)
+    torch.cuda.synchronize()
+    for a, b in zip(_mx_bytes(fused), _mx_bytes(unfused)):
+        assert np.array_equal(a, b)
+
+
+def _near_codes(gpu, ref):
+    """Same sign and at most one E4M3 step apart (codes are monotone in the
+    magnitude within a sign)."""
+    g = gpu.astype(np.int32)
+    r = ref.astype(np.int32)
+    same_sign = ((g ^ r) & 0x80) == 0
+    return same_sign & (np.abs((g & 0x7F) - (r & 0x7F)) <= 1)
+
+
+@pytest.mark.parametrize("t,f,seed", [(256, 1024, 21), (640, 512, 22)])
+def test_swiglu_quantize_vs_oracle(t, f, seed):
+    """Against the oracle: quantize(round_to_bf16(swiglu(h))).  The device
+    forms silu in fp32, so its bf16 activation may sit one bf16 step from the
+    oracle's (the allowance of the plain SwiGLU test); such an element can move
+    its code by one step, or its block's scale by one at a power of two.
+    Everything else must match exactly, and the moves must be rare."""
+    log(f"swiglu_quantize vs oracle {t}x{f}")
+    h = _swiglu_input(t, f, seed)
+    out = mx.swiglu_quantize(h.to("cuda"), mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    a_ref = om.round_to_bf16(osw.swiglu_fwd(f64(h)))
+    qr, sr = om.quantize_rowwise(a_ref)
+    qc, sc = om.quantize_colwise(a_ref, [t])
+    for q_gpu, s_gpu, q_ref, s_ref in ((u8(out.row_data), u8(out.row_scale), qr, sr),
+                                       (u8(out.col_data), u8(out.col_scale), qc, sc)):
+        ds = s_gpu.astype(np.int32) - s_ref.astype(np.int32)
+        assert np.abs(ds).max() <= 1
+        assert np.count_nonzero(ds) <= max(2, s_ref.size // 1000)
+        same_scale = np.repeat(ds == 0, 32, axis=1)
+        diff = (q_gpu != q_ref) & same_scale
+        assert _near_codes(q_gpu[diff], q_ref[diff]).all()
+        assert np.count_nonzero(diff) <= max(4, q_ref.size // 1000)
+    # the zeroed gate rows quantize to signed zeros with scale byte 0
+    assert np.array_equal(u8(out.row_scale)[:32], np.zeros((32, f // 32), np.uint8))
+    assert np.array_equal(u8(out.row_data)[:32], qr[:32])
+
+
+def test_swiglu_quantize_reuses_outputs():
+    log("swiglu_quantize reuses outputs")
+    h1 = _swiglu_input(256, 512, 31).to("cuda")
+    h2 = _swiglu_input(256, 512, 32).to("cuda")
+    out = mx.swiglu_quantize(h1)
+    ptrs = (out.row_data.data_ptr(), out.col_data.data_ptr())
+    out = mx.swiglu_quantize(h2, out=out)
+    ref = mx.group_quantize(mx.swiglu_fwd(h2), mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    assert (out.row_data.data_ptr(), out.col_data.data_ptr()) == ptrs
+    for a, b in zip(_mx_bytes(out), _mx_bytes(ref)):
+        assert np.array_equal(a, b)

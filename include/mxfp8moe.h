@@ -99,6 +99,12 @@ int32_t mxfp8_abi_version(void);
  *   usage  MXFP8_ROWWISE | MXFP8_COLWISE (at least one)
  *   q_row  [T, K] u8,  s_row [T, K/32] u8        (required iff ROWWISE)
  *   q_col  [K, T] u8,  s_col [K, T/32] u8        (required iff COLWISE)
+ *   noop_flag  NULL, or a device int32 read when the kernels run: non-zero
+ *          makes the call write nothing, so the outputs keep their previous
+ *          contents ([P3224] Greptile Summary and its test list: the group
+ *          quantize's noop flag, replayed in a CUDA graph).  A captured
+ *          graph can thereby skip re-quantizing weights that did not change;
+ *          the flag is set or cleared by the caller's own kernels.
  * The same call quantizes a grouped weight [G, N, K] viewed as [G*N, K]
  * (T = G*N); its column-wise copy is then [K, G*N], expert g being columns
  * [g*N, (g+1)*N).
@@ -106,7 +112,7 @@ int32_t mxfp8_abi_version(void);
  */
 mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint32_t usage,
                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                                  uint8_t* s_col, void* stream);
+                                  uint8_t* s_col, const int32_t* noop_flag, void* stream);
 
 /*
  * Bytes of device workspace that mxfp8_requant_colwise (with dbias) and

@@ -24,7 +24,8 @@ SIGNATURES = {
     "mxfp8_last_error": (ctypes.c_char_p, []),
     "mxfp8_abi_version": (c_i32, []),
     "mxfp8_dbias_workspace_bytes": (c_size, [c_i64, c_i64]),
-    "mxfp8_group_quantize": (c_i32, [c_vp, c_i64, c_i64, c_u32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "mxfp8_group_quantize": (c_i32, [c_vp, c_i64, c_i64, c_u32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp]),
     "mxfp8_requant_colwise": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_size, c_vp]),
     "mxfp8_grouped_dbias": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_size,
@@ -44,7 +45,7 @@ SIGNATURES = {
     "mxfp8_convert_sweep": (c_i32, [c_i32, c_vp, c_size, c_vp]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 MXFP8_OK, MXFP8_EINVAL, MXFP8_ENOTSUP, MXFP8_EHIP = 0, 1, 2, 3
 

@@ -109,15 +109,23 @@ def _mx_ptrs(out, usage):
             _ptr(out.col_data) if col else None, _ptr(out.col_scale) if col else None)
 
 
-def group_quantize(x, usage=ROWWISE, out: Optional[MXFP8Tensor] = None, stream=None):
-    """bf16 [T, K] (or [G, N, K], taken as [G*N, K]) -> MXFP8Tensor."""
+def group_quantize(x, usage=ROWWISE, out: Optional[MXFP8Tensor] = None, noop_flag=None,
+                   stream=None):
+    """bf16 [T, K] (or [G, N, K], taken as [G*N, K]) -> MXFP8Tensor.
+
+    noop_flag: optional device int32 [1]; when it holds a non-zero value as
+    the kernels run, nothing is written and `out` keeps its contents.
+    """
     lib = _lib()
     if x.dim() != 2:
         x = x.reshape(-1, x.shape[-1])
     t, k = x.shape
     _need(x, torch.bfloat16, (t, k), "x")
     out = _mx_outputs(out, usage, t, k, x)
-    st = lib.mxfp8_group_quantize(_ptr(x), t, k, usage, *_mx_ptrs(out, usage), _stream(stream))
+    if noop_flag is not None:
+        _need(noop_flag, torch.int32, (1,), "noop_flag")
+    st = lib.mxfp8_group_quantize(_ptr(x), t, k, usage, *_mx_ptrs(out, usage), _ptr(noop_flag),
+                                  _stream(stream))
     _native.check(st, "mxfp8_group_quantize")
     return out
 
@@ -200,23 +208,32 @@ def grouped_dbias(row_data, row_scale, m_splits, dbias=None, workspace=None, str
 
 
 def grouped_scaled_bias_grad(row_data, row_scale, m_splits, scales=None, bias=None,
-                             want_dbias=True, want_dscales=True, workspace=None, stream=None):
+                             want_dbias=True, want_dscales=True, workspace=None, out=None,
+                             stream=None):
     """Gradients of a routing-scaled bias from row-wise MXFP8 dY [T, N]:
     dbias [G, N] = sum over each expert's rows of scales[r] dY[r] (needs
     scales [T] fp32) and dscales [T] = dY[r] . bias[g] (needs bias [G, N]
-    fp32).  Returns (dbias or None, dscales or None)."""
+    fp32).  out: optional (dbias, dscales) buffers to write into.  Returns
+    (dbias or None, dscales or None)."""
     lib = _lib()
     t, n = row_data.shape
     _need(row_data, torch.uint8, (t, n), "row_data")
     _need(row_scale, torch.uint8, (t, n // 32), "row_scale")
     ms = _splits(m_splits)
     g = ms.numel()
-    dbias = _empty((g, n), torch.float32, row_data) if want_dbias else None
-    dscales = _empty((t,), torch.float32, row_data) if want_dscales else None
+    dbias, dscales = (None, None) if out is None else out
     if want_dbias:
         _need(scales, torch.float32, (t,), "scales")
+        dbias = _empty((g, n), torch.float32, row_data) if dbias is None else dbias
+        _need(dbias, torch.float32, (g, n), "dbias")
+    else:
+        dbias = None
     if want_dscales:
         _need(bias, torch.float32, (g, n), "bias")
+        dscales = _empty((t,), torch.float32, row_data) if dscales is None else dscales
+        _need(dscales, torch.float32, (t,), "dscales")
+    else:
+        dscales = None
     need = lib.mxfp8_scaled_bias_workspace_bytes(t, n)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=row_data.device)

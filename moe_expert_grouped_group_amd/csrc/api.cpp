@@ -67,7 +67,7 @@ extern "C" {
 
 const char* mxfp8_last_error(void) { return g_err; }
 
-int32_t mxfp8_abi_version(void) { return 1; }
+int32_t mxfp8_abi_version(void) { return 2; }
 
 size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0) return 0;
@@ -76,7 +76,7 @@ size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N) {
 
 mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint32_t usage,
                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                                  uint8_t* s_col, void* stream) {
+                                  uint8_t* s_col, const int32_t* noop_flag, void* stream) {
   const char* fn = "mxfp8_group_quantize";
   REQUIRE(x != nullptr, "%s: x is NULL", fn);
   REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
@@ -91,9 +91,9 @@ mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint3
   hipError_t e;
   if (col)
     e = mx::launch_quant_rowcol(x, T, K, row ? q_row : nullptr, row ? s_row : nullptr, q_col,
-                                s_col, as_stream(stream));
+                                s_col, noop_flag, as_stream(stream));
   else
-    e = mx::launch_quant_rowwise(x, T, K, q_row, s_row, as_stream(stream));
+    e = mx::launch_quant_rowwise(x, T, K, q_row, s_row, noop_flag, as_stream(stream));
   return hip_status(e, fn);
 }
 

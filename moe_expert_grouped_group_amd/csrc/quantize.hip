@@ -77,6 +77,12 @@ __device__ __forceinline__ uint2 encode_chunk(uint4 w, uint32_t byte) {
   return make_uint2(cvt4_bf16_e4m3(w.x, w.y, sc), cvt4_bf16_e4m3(w.z, w.w, sc));
 }
 
+// A launch whose device no-op flag is set writes nothing (outputs keep their
+// contents), so that a captured graph can skip re-quantizing unchanged data.
+__device__ __forceinline__ bool skip_launch(const int32_t* noop) {
+  return noop != nullptr && *noop != 0;
+}
+
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
 
@@ -85,7 +91,8 @@ constexpr int kRowUnroll = 4;
 // order because K % 32 == 0).  nchunks is a multiple of 256.
 __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ s,
-    int64_t nchunks) {
+    int64_t nchunks, const int32_t* __restrict__ noop) {
+  if (skip_launch(noop)) return;
   const int64_t stride = (int64_t)gridDim.x * kRowThreads * kRowUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kRowThreads * kRowUnroll + threadIdx.x;
        base < nchunks; base += stride) {
@@ -297,8 +304,9 @@ __device__ __forceinline__ void colwise_pass_bf16(const uint8_t* lds, int64_t T,
 __global__ __launch_bounds__(kColThreads) void quant_rowcol_kernel(
     const uint16_t* __restrict__ x, int64_t T, int64_t K, uint8_t* __restrict__ q_row,
     uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-    int32_t ntk, int32_t ntiles) {
+    int32_t ntk, int32_t ntiles, const int32_t* __restrict__ noop) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytesBf16];
+  if (skip_launch(noop)) return;
   const int tid = threadIdx.x;
   int tile = blockIdx.x;
   u32x4 w[8];
@@ -946,11 +954,11 @@ static int grid_for(int64_t work_items, int per_block, int cap) {
 }
 
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t T, int64_t K, uint8_t* q, uint8_t* s,
-                                hipStream_t st) {
+                                const int32_t* noop, hipStream_t st) {
   const int64_t nchunks = T * K / 8;
   const int grid = grid_for(nchunks, kRowThreads * kRowUnroll, 256 * 16);
   hipLaunchKernelGGL(quant_rowwise_kernel, dim3(grid), dim3(kRowThreads), 0, st,
-                     reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q), s, nchunks);
+                     reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q), s, nchunks, noop);
   return hipGetLastError();
 }
 
@@ -968,12 +976,13 @@ constexpr int kRowcolWgPerCu = 4;
 constexpr int kRequantWgPerCu = 5;
 
 hipError_t launch_quant_rowcol(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
-                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st) {
+                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                               const int32_t* noop, hipStream_t st) {
   const int32_t ntt = (int32_t)(T / kTileT), ntk = (int32_t)(K / kTileK);
   const int32_t ntiles = ntt * ntk;
   const int grid = (int)std::min<int64_t>(ntiles, (int64_t)device_cus() * kRowcolWgPerCu);
   hipLaunchKernelGGL(quant_rowcol_kernel, dim3(grid), dim3(kColThreads), 0, st, x, T, K, q_row,
-                     s_row, q_col, s_col, ntk, ntiles);
+                     s_row, q_col, s_col, ntk, ntiles, noop);
   return hipGetLastError();
 }
 

@@ -57,15 +57,15 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 def test_quantize_rejects(lib):
     q = lib.mxfp8_group_quantize
-    assert _status_msg(lib, q(None, 128, 512, 1, FAKE, FAKE, None, None, None))[0] == 1
-    st, msg = _status_msg(lib, q(FAKE, 100, 512, 1, FAKE, FAKE, None, None, None))
+    assert _status_msg(lib, q(None, 128, 512, 1, FAKE, FAKE, None, None, None, None))[0] == 1
+    st, msg = _status_msg(lib, q(FAKE, 100, 512, 1, FAKE, FAKE, None, None, None, None))
     assert st == 1 and "128" in msg
-    st, msg = _status_msg(lib, q(FAKE, 128, 96, 1, FAKE, FAKE, None, None, None))
+    st, msg = _status_msg(lib, q(FAKE, 128, 96, 1, FAKE, FAKE, None, None, None, None))
     assert st == 1 and "512" in msg
-    assert q(FAKE, 128, 512, 0, FAKE, FAKE, None, None, None) == 1          # no usage
-    assert q(FAKE, 128, 512, 4, FAKE, FAKE, None, None, None) == 1          # unknown usage bit
-    assert q(FAKE, 128, 512, 2, FAKE, FAKE, None, None, None) == 1          # col without buffers
-    assert q(FAKE, 128, 512, 1, None, FAKE, None, None, None) == 1          # row without data
+    assert q(FAKE, 128, 512, 0, FAKE, FAKE, None, None, None, None) == 1          # no usage
+    assert q(FAKE, 128, 512, 4, FAKE, FAKE, None, None, None, None) == 1          # unknown usage bit
+    assert q(FAKE, 128, 512, 2, FAKE, FAKE, None, None, None, None) == 1          # col without buffers
+    assert q(FAKE, 128, 512, 1, None, FAKE, None, None, None, None) == 1          # row without data
 
 
 def test_gemm_rejects(lib):

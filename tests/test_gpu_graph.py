@@ -112,3 +112,119 @@ def test_graph_replay_matches_eager():
             b = want.view(torch.uint8) if want.dtype == torch.float32 else want
             assert torch.equal(a, b), f"replay {i}: {name} differs from the eager run"
         del ref
+
+
+class _FrozenStep:
+    """The step with frozen expert weights ("[Pytorch] Add support for row-wise
+    quanted input for grouped gemm", Greptile Summary: with frozen weights the
+    backward still gives the input gradient and the ordinary and scaled-bias
+    gradients, reduced straight from the dequantized dY, with no wgrad stage).
+    No column-wise copy of X is made and no wgrad runs.  The weight quantize
+    takes a device no-op flag: with the weights unchanged, a replay can skip
+    it and keep the previous copies ("Improve device-init grouped linear
+    module with single grouped weight support", Greptile Summary: the noop
+    path of the group quantize under CUDA-graph replay)."""
+
+    def __init__(self, w, x, wt, dy, scales, bias):
+        g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+        u8 = dict(dtype=torch.uint8, device="cuda")
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.shape = (g, t, k, n)
+        self.ms = torch.from_numpy(w.m_splits).to("cuda")
+        self.x, self.wt, self.dy = x.to("cuda"), wt.to("cuda"), dy.to("cuda")
+        self.scales, self.bias = scales.to("cuda"), bias.to("cuda")
+        self.noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.xo = mx.MXFP8Tensor(torch.empty(t, k, **u8), torch.empty(t, k // 32, **u8))
+        self.wo = mx.MXFP8Tensor(torch.empty(g * n, k, **u8), torch.empty(g * n, k // 32, **u8),
+                                 torch.empty(k, g * n, **u8), torch.empty(k, g * n // 32, **u8))
+        self.dyo = mx.MXFP8Tensor(torch.empty(t, n, **u8), torch.empty(t, n // 32, **u8))
+        self.y = torch.empty(t, n, **f32)
+        self.dx = torch.empty(t, k, **f32)
+        self.db = torch.empty(g, n, **f32)
+        self.sdb = torch.empty(g, n, **f32)
+        self.dsc = torch.empty(t, **f32)
+        self.ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8)
+        lib = mx.load_library()
+        self.sws = torch.empty(lib.mxfp8_scaled_bias_workspace_bytes(t, n), **u8)
+
+    def run(self):
+        g, t, k, n = self.shape
+        ms = self.ms
+        mx.group_quantize(self.wt, mx.ROWWISE | mx.COLWISE, out=self.wo, noop_flag=self.noop)
+        mx.group_quantize(self.x, mx.ROWWISE, out=self.xo)
+        mx.grouped_gemm("NT", self.xo.row_data, self.xo.row_scale, self.wo.row_data,
+                        self.wo.row_scale, ms, t, n, k, torch.float32, self.y)
+        mx.group_quantize(self.dy, mx.ROWWISE, out=self.dyo)
+        mx.grouped_gemm("NN", self.dyo.row_data, self.dyo.row_scale, self.wo.col_data,
+                        self.wo.col_scale, ms, t, n, k, torch.float32, self.dx)
+        mx.grouped_dbias(self.dyo.row_data, self.dyo.row_scale, ms, dbias=self.db,
+                         workspace=self.ws)
+        mx.grouped_scaled_bias_grad(self.dyo.row_data, self.dyo.row_scale, ms, self.scales,
+                                    self.bias, out=(self.sdb, self.dsc), workspace=self.sws)
+
+    def outputs(self):
+        return {"w_row": self.wo.row_data, "w_col": self.wo.col_data, "y": self.y,
+                "dx": self.dx, "dbias": self.db, "scaled_dbias": self.sdb, "dscales": self.dsc}
+
+
+def _routing(w, i):
+    rng = np.random.default_rng([w.wid, 300 + i])
+    scales = torch.from_numpy(rng.random(w.tokens).astype(np.float32))
+    bias = torch.from_numpy(rng.standard_normal((w.groups, w.ffn)).astype(np.float32))
+    return scales, bias
+
+
+def _same(got, want, what):
+    for name, b in want.items():
+        a = got[name]
+        a = a.view(torch.uint8) if a.dtype == torch.float32 else a
+        b = b.view(torch.uint8) if b.dtype == torch.float32 else b
+        assert torch.equal(a, b), f"{what}: {name} differs"
+
+
+def test_frozen_weight_step_with_noop_weight_quantize():
+    """Replays of the frozen-weight step: with the no-op flag clear the
+    weights are re-quantized from the captured buffer; with it set they keep
+    the last copies even though the buffer now holds other weights.  Each
+    replay equals, byte for byte, an eager frozen step on the inputs it should
+    have used; its dX also equals the full step's."""
+    w = wl.make("small_moe8")
+    x0, wt0, dy0 = _inputs(w, 0)
+    sc, bi = _routing(w, 0)
+    cap = _FrozenStep(w, x0, wt0, dy0, sc, bi)
+    log("frozen graph: warm-up on a side stream")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cap.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("frozen graph: capture")
+    with torch.cuda.graph(graph):
+        cap.run()
+    torch.cuda.synchronize()
+    # (flag, step inputs, weights the copies must come from)
+    x1, wt1, dy1 = _inputs(w, 1)
+    x2, wt2, dy2 = _inputs(w, 2)
+    x3, _, dy3 = _inputs(w, 3)
+    plan = [(0, (x1, wt1, dy1), wt1), (1, (x2, wt2, dy2), wt1), (0, (x3, wt2, dy3), wt2)]
+    for i, (flag, (x, wt, dy), w_used) in enumerate(plan, start=1):
+        cap.noop.fill_(flag)
+        cap.x.copy_(x.to("cuda"))
+        cap.wt.copy_(wt.to("cuda"))
+        cap.dy.copy_(dy.to("cuda"))
+        log(f"frozen graph: replay {i} noop {flag}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in cap.outputs().items()}
+        log(f"frozen graph: eager run {i}")
+        ref = _FrozenStep(w, x, w_used, dy, sc, bi)
+        ref.run()
+        full = _Step(w, x, w_used, dy)
+        full.run()
+        torch.cuda.synchronize()
+        _same(got, ref.outputs(), f"replay {i}")
+        _same({"dx": got["dx"], "y": got["y"]}, {"dx": full.dx, "y": full.y},
+              f"replay {i} vs the full step")
+        del ref, full

@@ -338,3 +338,29 @@ def test_swiglu_quantize_reuses_outputs():
     assert (out.row_data.data_ptr(), out.col_data.data_ptr()) == ptrs
     for a, b in zip(_mx_bytes(out), _mx_bytes(ref)):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("usage", [mx.ROWWISE, mx.COLWISE, mx.ROWWISE | mx.COLWISE])
+def test_noop_flag(usage):
+    """A set no-op flag leaves every output as the last call wrote it; a
+    cleared one quantizes as usual (both kernels: row-wise only, and the
+    row + column kernel)."""
+    log(f"noop flag usage {usage}")
+    x1 = bf16_from_bits(sweep_bf16_bits(256, 1024, 41))
+    x2 = bf16_from_bits(sweep_bf16_bits(256, 1024, 42))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = mx.group_quantize(x1.to("cuda"), usage, noop_flag=flag)
+    flag.fill_(1)
+    out = mx.group_quantize(x2.to("cuda"), usage, out=out, noop_flag=flag)
+    torch.cuda.synchronize()
+    if usage & mx.ROWWISE:
+        _check_row(x1, out)
+    if usage & mx.COLWISE:
+        _check_col(x1, out)
+    flag.fill_(0)
+    out = mx.group_quantize(x2.to("cuda"), usage, out=out, noop_flag=flag)
+    torch.cuda.synchronize()
+    if usage & mx.ROWWISE:
+        _check_row(x2, out)
+    if usage & mx.COLWISE:
+        _check_col(x2, out)

@@ -550,82 +550,96 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 
     // Two MFMA steps per stage st, 16 MFMAs per wave each, every MFMA
     // followed by at most one fragment read and a copy or two (with one wave
-    // per SIMD, more between two MFMAs idles the matrix pipe).
+    // per SIMD, more between two MFMAs idles the matrix pipe).  The 16 copies
+    // of stage st + 2 go into slot st % 2 as soon as every wave has read it,
+    // spread over a step and a half, so the copy path is never flooded by all
+    // of them within one step (3-7 % faster than issuing all 16 in the odd
+    // step).
     // Even step 2 st: MFMAs on set 0 (step 2 st); reads of step 2 st + 1
-    // (second half of stage st, already resident) into set 1.
-    // Odd step 2 st + 1: this wave waits for its LDS reads of stage st and
-    // for all its copies (stage st + 1 is the newest one), then the barrier
-    // makes stage st + 1 visible and frees slot st % 2; MFMAs on set 1; reads
-    // of step 2 st + 2 (stage st + 1) into set 0; the 16 copies of stage
-    // st + 2 into the freed slot, two steps ahead of their first read, and
-    // the scale group that starts there.
-#define MX_EVEN(ST, FULL)                                                                   \
+    // (second half of stage st) into set 1 after the first 8 MFMAs; then this
+    // wave's reads are waited for and the barrier frees slot st % 2 (no wave
+    // reads stage st after it); 6 copies of stage st + 2 into it.
+    // Odd step 2 st + 1: this wave waits for its copies of stage st + 1 (only
+    // the 6 just issued may still be in flight: the counter completes in issue
+    // order), then the barrier makes stage st + 1 visible; MFMAs on set 1;
+    // reads of step 2 st + 2 (stage st + 1) into set 0; the other 10 copies
+    // of stage st + 2 and the scale group that starts there.  Every copy of
+    // stage st + 2 has at least the whole even step 2 st + 2 to land before
+    // the wait of odd step 2 st + 3.
+#define MX_EVEN(ST, FULL, CP)                                                               \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
+    const bool pf_ = (FULL) || st_ + 2 < ns;                                                \
     const StepRead rd_ = step_read(2 * st_ + 1);                                            \
     MX_FENCE                                                                                \
     MX_MFMA(0, 0, 0) load_a(rd_, 1, 0); MX_FENCE                                            \
-    MX_MFMA(0, 1, 0)                                                                        \
-    MX_MFMA(0, 2, 0) load_b(rd_, 1, 0); MX_FENCE                                            \
-    MX_MFMA(0, 3, 0)                                                                        \
-    MX_MFMA(1, 0, 0) load_a(rd_, 1, 1); MX_FENCE                                            \
-    MX_MFMA(1, 1, 0)                                                                        \
-    MX_MFMA(1, 2, 0) load_b(rd_, 1, 1); MX_FENCE                                            \
-    MX_MFMA(1, 3, 0)                                                                        \
-    MX_MFMA(2, 0, 0) load_a(rd_, 1, 2); MX_FENCE                                            \
-    MX_MFMA(2, 1, 0)                                                                        \
-    MX_MFMA(2, 2, 0) load_b(rd_, 1, 2); MX_FENCE                                            \
-    MX_MFMA(2, 3, 0)                                                                        \
-    MX_MFMA(3, 0, 0) load_a(rd_, 1, 3); MX_FENCE                                            \
-    MX_MFMA(3, 1, 0)                                                                        \
-    MX_MFMA(3, 2, 0) load_b(rd_, 1, 3); MX_FENCE                                            \
-    MX_MFMA(3, 3, 0)                                                                        \
+    MX_MFMA(0, 1, 0) load_b(rd_, 1, 0); MX_FENCE                                            \
+    MX_MFMA(0, 2, 0) load_a(rd_, 1, 1); MX_FENCE                                            \
+    MX_MFMA(0, 3, 0) load_b(rd_, 1, 1); MX_FENCE                                            \
+    MX_MFMA(1, 0, 0) load_a(rd_, 1, 2); MX_FENCE                                            \
+    MX_MFMA(1, 1, 0) load_b(rd_, 1, 2); MX_FENCE                                            \
+    MX_MFMA(1, 2, 0) load_a(rd_, 1, 3); MX_FENCE                                            \
+    MX_MFMA(1, 3, 0) load_b(rd_, 1, 3); MX_FENCE                                            \
+    MX_MFMA(2, 0, 0)                                                                        \
+    if (pf_) {                                                                              \
+      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage st */  \
+      __syncthreads();                    /* slot st % 2 is free */                         \
+    }                                                                                       \
+    MX_FENCE                                                                                \
+    MX_MFMA(2, 1, 0) if (pf_) copy_a(CP); MX_FENCE                                          \
+    MX_MFMA(2, 2, 0) if (pf_) copy_b(CP); MX_FENCE                                          \
+    MX_MFMA(2, 3, 0) MX_FENCE                                                               \
+    MX_MFMA(3, 0, 0) if (pf_) copy_a(CP); MX_FENCE                                          \
+    MX_MFMA(3, 1, 0) if (pf_) copy_b(CP); MX_FENCE                                          \
+    MX_MFMA(3, 2, 0) MX_FENCE                                                               \
+    MX_MFMA(3, 3, 0) if (pf_) copy_a(CP); if (pf_) copy_b(CP); MX_FENCE                     \
   }
-#define MX_ODD(ST, FULL)                                                                         \
+#define MX_ODD(ST, FULL, CP)                                                                \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
     const bool nx_ = (FULL) || st_ + 1 < ns;                                                \
     const bool pf_ = (FULL) || st_ + 2 < ns;                                                \
     const bool sg_ = pf_ && (((st_ + 2) * 2) % kScaleSteps == 0);                           \
     const int g_ = ((st_ + 2) * 2) / kScaleSteps;                                           \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage st */    \
     if (nx_) {                                                                              \
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                             \
+      /* stage st + 1 landed; only the 6 copies of stage st + 2 may be pending */          \
+      if (pf_) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));                                    \
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                        \
       __syncthreads();                                                                      \
     }                                                                                       \
     const StepRead rd_ = step_read(2 * st_ + 2);                                            \
-    StageCopy cp_ = stage_copy(st_ + 2);                                                    \
     MX_FENCE                                                                                \
-    MX_MFMA(0, 0, 1) if (nx_) load_a(rd_, 0, 0); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(0, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(0, 2, 1) if (nx_) load_b(rd_, 0, 0); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(0, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(1, 0, 1) if (nx_) load_a(rd_, 0, 1); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(1, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(1, 2, 1) if (nx_) load_b(rd_, 0, 1); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(1, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(2, 0, 1) if (nx_) load_a(rd_, 0, 2); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(2, 1, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); if (pf_) copy_a(cp_); MX_FENCE             \
-    MX_MFMA(2, 3, 1) if (pf_) copy_b(cp_); MX_FENCE                                         \
-    MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (pf_) copy_a(cp_);                      \
+    MX_MFMA(0, 0, 1) if (nx_) load_a(rd_, 0, 0); if (pf_) copy_a(CP); MX_FENCE              \
+    MX_MFMA(0, 1, 1) if (pf_) copy_b(CP); MX_FENCE                                          \
+    MX_MFMA(0, 2, 1) if (nx_) load_b(rd_, 0, 0); MX_FENCE                                   \
+    MX_MFMA(0, 3, 1) if (pf_) copy_a(CP); MX_FENCE                                          \
+    MX_MFMA(1, 0, 1) if (nx_) load_a(rd_, 0, 1); if (pf_) copy_b(CP); MX_FENCE              \
+    MX_MFMA(1, 1, 1) MX_FENCE                                                               \
+    MX_MFMA(1, 2, 1) if (nx_) load_b(rd_, 0, 1); if (pf_) copy_a(CP); MX_FENCE              \
+    MX_MFMA(1, 3, 1) if (pf_) copy_b(CP); MX_FENCE                                          \
+    MX_MFMA(2, 0, 1) if (nx_) load_a(rd_, 0, 2); MX_FENCE                                   \
+    MX_MFMA(2, 1, 1) if (pf_) copy_a(CP); MX_FENCE                                          \
+    MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); if (pf_) copy_b(CP); MX_FENCE              \
+    MX_MFMA(2, 3, 1) MX_FENCE                                                               \
+    MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (pf_) copy_a(CP);                       \
     if (sg_) scale_part(g_, 0); MX_FENCE                                                    \
-    MX_MFMA(3, 1, 1) if (pf_) copy_b(cp_); if (sg_) scale_part(g_, 1); MX_FENCE             \
-    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (pf_) copy_a(cp_);                      \
-    if (sg_) scale_part(g_, 2); MX_FENCE                                                    \
-    MX_MFMA(3, 3, 1) if (pf_) copy_b(cp_); if (sg_) scale_part(g_, 3); MX_FENCE             \
+    MX_MFMA(3, 1, 1) if (pf_) copy_b(CP); if (sg_) scale_part(g_, 1); MX_FENCE              \
+    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (sg_) scale_part(g_, 2); MX_FENCE       \
+    MX_MFMA(3, 3, 1) if (sg_) scale_part(g_, 3); MX_FENCE                                   \
   }
 
     // steady state (every stage has a successor two ahead), then the last
     // two stages with those checks
     int st = 0;
     for (; st + 2 < ns; ++st) {
-      MX_EVEN(st, true)
-      MX_ODD(st, true)
+      StageCopy cp = stage_copy(st + 2);
+      MX_EVEN(st, true, cp)
+      MX_ODD(st, true, cp)
     }
     for (; st < ns; ++st) {
-      MX_EVEN(st, false)
-      MX_ODD(st, false)
+      StageCopy cp = stage_copy(st + 2);
+      MX_EVEN(st, false, cp)
+      MX_ODD(st, false, cp)
     }
 #undef MX_EVEN
 #undef MX_ODD

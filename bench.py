@@ -23,7 +23,14 @@ and WRITE_SIZE counter summary under profiles/, scaled by the same counters
 read on a plain device copy of known size (--calibrate-copy); it is reported
 only while the GEMM source still hashes to the one the counters were taken on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+After the headline step, the other workloads of the same path are timed the
+same way (fewer steps) and reported under "other_workloads": the skewed
+128-expert linear (hidden 7168 -> 2048, 38 experts without tokens), the fused
+expert MLP forward and backward (64 experts, 83968 tokens, 3072 -> 2048 ->
+SwiGLU -> 1024 -> 3072, bf16 outputs) and the standalone row + column-wise
+group quantize of 131072 x 7168.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
        python bench.py --calibrate-copy      (copy of 1 GiB, for counter scaling)
 """
 
@@ -53,6 +60,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads (skewed 128-expert linear, fused MLP, "
+                         "standalone group quantize)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (counter scaling)")
     return ap.parse_args()
@@ -162,6 +172,204 @@ def _time_outside(fn, steps):
         pairs.append((a, b))
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def _run_steps(launches, steps, warmup):
+    """Time a step made of named launches: warmup steps, then `steps` steps
+    between two events; every launch also bracketed by its own events.
+    Returns (ms per step, {name: mean ms per launch})."""
+    import numpy as np
+    import torch
+
+    ev = {}
+
+    def step():
+        for name, fn in launches:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.setdefault(name, []).append((a, b))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev.clear()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    per = {nm: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for nm, pairs in ev.items()}
+    return start.elapsed_time(stop) / steps, per
+
+
+def _gemm_roofline_ms(flops, bytes_):
+    """Time bound of one GEMM launch: the larger of its flops at the MFMA peak
+    and its algorithmic bytes at the HBM peak."""
+    return max(flops / (PEAK_MXFP8_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+
+
+def bench_skewed_linear(steps, warmup):
+    """128 experts (38 without tokens), hidden 7168 -> 2048, 32768 tokens, X
+    with 0.1 % outliers x1000, fp32 outputs.  X arrives row-wise quantized
+    (its quantize is not in the step); the weight is quantized in the step."""
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    w = wl.make("skewed_dsv3")
+    g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    ms = torch.from_numpy(w.m_splits).cuda()
+    x, wt, dy = (w.tensors[nm].cuda() for nm in ("x", "w", "dy"))
+    xo = mx.group_quantize(x, mx.ROWWISE)
+    wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE)
+    xc = mx.requant_colwise(xo.row_data, xo.row_scale)
+    dyo = mx.group_quantize(dy, mx.ROWWISE)
+    dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True)
+    f32 = torch.float32
+    y = torch.empty(t, n, dtype=f32, device="cuda")
+    dx = torch.empty(t, k, dtype=f32, device="cuda")
+    dw = torch.empty(g, n, k, dtype=f32, device="cuda")
+    ws = torch.empty(mx.dbias_workspace_bytes(t, n), dtype=torch.uint8, device="cuda")
+    launches = [
+        ("quant_w", lambda: mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo)),
+        ("gemm_fprop", lambda: mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data,
+                                               wo.row_scale, ms, t, n, k, f32, y)),
+        ("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)),
+        ("quant_dy", lambda: mx.group_quantize(dy, mx.ROWWISE, out=dyo)),
+        ("gemm_dgrad", lambda: mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data,
+                                               wo.col_scale, ms, t, n, k, f32, dx)),
+        ("requant_dy_dbias", lambda: mx.requant_colwise(dyo.row_data, dyo.row_scale, ms,
+                                                        with_dbias=True, out=dyc, dbias=db,
+                                                        workspace=ws)),
+        ("gemm_wgrad", lambda: mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data,
+                                               xc.col_scale, ms, t, n, k, f32, dw)),
+    ]
+    ms_step, per = _run_steps(launches, steps, warmup)
+    flop = 2.0 * t * n * k
+    busy = int((w.m_splits > 0).sum())
+    sc = 1 + 1 / 32
+    # algorithmic bytes: A and B (experts with tokens) codes + scales, C once
+    gbytes = {"gemm_fprop": t * k * sc + busy * n * k * sc + t * n * 4,
+              "gemm_dgrad": t * n * sc + busy * n * k * sc + t * k * 4,
+              "gemm_wgrad": t * n * sc + t * k * sc + g * n * k * 4}
+    gemm_ms = sum(per[nm] for nm in gbytes)
+    bound_ms = sum(_gemm_roofline_ms(flop, b) for b in gbytes.values())
+    return {
+        "experts": g, "empty_experts": int((w.m_splits == 0).sum()), "tokens": t, "hidden": k,
+        "ffn": n, "out_dtype": "f32", "ms_per_step": round(ms_step, 4),
+        "tflops_step": round(3 * flop / (ms_step * 1e-3) / 1e12, 2),
+        "gemm_tflops": round(3 * flop / (gemm_ms * 1e-3) / 1e12, 2),
+        "gemm_roofline_frac": round(bound_ms / gemm_ms, 4),
+        "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
+        "note": "X pre-quantized row-wise (not in the step); gemm_roofline_frac = sum over the "
+                "three GEMMs of max(flops / MFMA peak, algorithmic bytes / HBM peak) over their "
+                "measured time (the fp32 wgrad output makes it HBM-bound)",
+    }
+
+
+def bench_fused_mlp(steps, warmup):
+    """Fused expert MLP, forward and backward: 64 experts, 83968 tokens,
+    hidden 3072, FC1 3072 -> 2048 (gate | up), SwiGLU to 1024, FC2 1024 ->
+    3072, bf16 GEMM outputs; only column-wise copies of X and of the SwiGLU
+    output are kept for the backward."""
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    w = wl.make("nemotron_proxy_mlp")
+    g, t, k, n2 = w.groups, w.tokens, w.hidden, w.ffn
+    f = n2 // 2
+    ms = torch.from_numpy(w.m_splits).cuda()
+    x, w1, w2, dout = (w.tensors[nm].cuda() for nm in ("x", "w", "w2", "dy"))
+    del w
+    bf = torch.bfloat16
+    R, C = mx.ROWWISE, mx.COLWISE
+    xo = mx.group_quantize(x, R)
+    w1o = mx.group_quantize(w1, R | C)
+    w2o = mx.group_quantize(w2, R | C)
+    h = torch.empty(t, n2, dtype=bf, device="cuda")
+    ao = mx.swiglu_quantize(torch.zeros(t, n2, dtype=bf, device="cuda"), R | C)
+    y = torch.empty(t, k, dtype=bf, device="cuda")
+    xc = mx.requant_colwise(xo.row_data, xo.row_scale)
+    dyo = mx.group_quantize(dout, R)
+    dyc = mx.requant_colwise(dyo.row_data, dyo.row_scale)
+    da = torch.empty(t, f, dtype=bf, device="cuda")
+    dw2 = torch.empty(g, k, f, dtype=bf, device="cuda")
+    dh = torch.empty(t, n2, dtype=bf, device="cuda")
+    dho = mx.group_quantize(dh.zero_(), R)
+    dhc, db1 = mx.requant_colwise(dho.row_data, dho.row_scale, ms, with_dbias=True)
+    dx = torch.empty(t, k, dtype=bf, device="cuda")
+    dw1 = torch.empty(g, n2, k, dtype=bf, device="cuda")
+    ws = torch.empty(mx.dbias_workspace_bytes(t, n2), dtype=torch.uint8, device="cuda")
+    gemm = mx.grouped_gemm
+    launches = [
+        ("quant_x", lambda: mx.group_quantize(x, R, out=xo)),
+        ("quant_w1", lambda: mx.group_quantize(w1, R | C, out=w1o)),
+        ("quant_w2", lambda: mx.group_quantize(w2, R | C, out=w2o)),
+        ("fc1_fprop", lambda: gemm("NT", xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale,
+                                   ms, t, n2, k, bf, h)),
+        ("swiglu_quant", lambda: mx.swiglu_quantize(h, R | C, out=ao)),
+        ("fc2_fprop", lambda: gemm("NT", ao.row_data, ao.row_scale, w2o.row_data, w2o.row_scale,
+                                   ms, t, k, f, bf, y)),
+        ("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)),
+        ("quant_dy", lambda: mx.group_quantize(dout, R, out=dyo)),
+        ("fc2_dgrad", lambda: gemm("NN", dyo.row_data, dyo.row_scale, w2o.col_data,
+                                   w2o.col_scale, ms, t, k, f, bf, da)),
+        ("requant_dy", lambda: mx.requant_colwise(dyo.row_data, dyo.row_scale, out=dyc)),
+        ("fc2_wgrad", lambda: gemm("TN", dyc.col_data, dyc.col_scale, ao.col_data, ao.col_scale,
+                                   ms, t, k, f, bf, dw2)),
+        ("swiglu_bwd", lambda: mx.swiglu_bwd(h, da, out=dh)),
+        ("quant_dh", lambda: mx.group_quantize(dh, R, out=dho)),
+        ("fc1_dgrad", lambda: gemm("NN", dho.row_data, dho.row_scale, w1o.col_data,
+                                   w1o.col_scale, ms, t, n2, k, bf, dx)),
+        ("requant_dh_dbias", lambda: mx.requant_colwise(dho.row_data, dho.row_scale, ms,
+                                                        with_dbias=True, out=dhc, dbias=db1,
+                                                        workspace=ws)),
+        ("fc1_wgrad", lambda: gemm("TN", dhc.col_data, dhc.col_scale, xc.col_data, xc.col_scale,
+                                   ms, t, n2, k, bf, dw1)),
+    ]
+    ms_step, per = _run_steps(launches, steps, warmup)
+    flops = 3 * 2.0 * t * k * n2 + 3 * 2.0 * t * f * k
+    gemm_ms = sum(v for nm, v in per.items() if nm.startswith("fc"))
+    return {
+        "experts": g, "empty_experts": int((ms == 0).sum().item()), "tokens": t, "hidden": k,
+        "fc1_out": n2, "fc2_in": f, "out_dtype": "bf16", "tflop_per_step": round(flops / 1e12, 4),
+        "ms_per_step": round(ms_step, 4),
+        "tflops_step": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "gemm_frac_of_peak": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
+        "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
+    }
+
+
+def bench_group_quantize(steps, warmup):
+    """Standalone row + column-wise group quantize of a 131072 x 7168 bf16
+    tensor (256 experts, Student-t(3) values, 1 % zero tiles)."""
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    w = wl.make("group_quantize_131072x7168")
+    t, k = w.tokens, w.hidden
+    x = w.tensors["x"].cuda()
+    del w
+    out = mx.group_quantize(x, mx.ROWWISE | mx.COLWISE)
+    ms_step, per = _run_steps(
+        [("quant_rowcol", lambda: mx.group_quantize(x, mx.ROWWISE | mx.COLWISE, out=out))],
+        steps, warmup)
+    nbytes = t * k * (2 + 2 * (1 + 1 / 32))
+    gbs = nbytes / (per["quant_rowcol"] * 1e-3) / 1e9
+    return {"tokens": t, "hidden": k, "experts": 256, "ms": round(per["quant_rowcol"], 4),
+            "algorithmic_bytes": int(nbytes), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -345,6 +553,19 @@ def main():
                               "frac": round(quant_gbs / PEAK_HBM_GBS, 4)},
         "wall_s": round(wall, 3),
     }
+    if not args.no_others:
+        # the other workloads, each timed the same way (fewer steps), outside
+        # the headline step
+        del x, wt, dy, xo, wo, xc, dyo, dyc, y, dx, dw, db, ws, r_scales, r_bias, sb_ws
+        torch.cuda.empty_cache()
+        o_steps, o_warm = max(3, min(args.steps, 10)), max(1, min(args.warmup, 2))
+        others = {}
+        for name, fn in (("skewed_dsv3", bench_skewed_linear),
+                         ("nemotron_proxy_mlp", bench_fused_mlp),
+                         ("group_quantize_131072x7168", bench_group_quantize)):
+            others[name] = fn(o_steps, o_warm)
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

@@ -309,9 +309,22 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.nblk = (int32_t)(p.kc / 32);
     d.c = reinterpret_cast<char*>(p.c) + (m0c * p.ldc + n0) * esz;
   } else {
+    // The list of tiles (experts in decreasing order of tokens) is consumed
+    // from both ends at once: of the two workgroups of a pair (tiles 2q and
+    // 2q + 1), one takes position q and the other position ntiles - 1 - q,
+    // and they swap ends every round of the grid.  Every workgroup then
+    // alternates a long tile with a short one, so the output stores of the
+    // short tiles (few contraction steps, a whole 256 x 256 output) overlap
+    // the other workgroups' contraction instead of all falling at the end.
+    // Both tiles of a pair lie in the same round (g2 is even), so the map is
+    // a bijection of [0, ntiles); with ntiles odd the last tile is the middle.
+    const int g2 = (int)((gridDim.x + 1) & ~1u);
+    const int q = tile >> 1;
+    const int from_back = (tile & 1) ^ ((tile / g2) & 1);
+    const int pos = from_back ? p.ntiles - 1 - q : q;
     const int per_expert = p.band * p.ntiles_n;
-    const int g = t->order[tile / per_expert];
-    const int rem = tile % per_expert;
+    const int g = t->order[pos / per_expert];
+    const int rem = pos % per_expert;
     const int mtl = rem / p.ntiles_n, nt = rem % p.ntiles_n;
     // p.kc = T here.  Runs are multiples of 128 tokens by contract; rounding
     // down keeps every copy inside [0, T) and aligned for any split values.

@@ -34,6 +34,7 @@ namespace mx {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   us2 x = __builtin_bit_cast(us2, a);
@@ -134,7 +135,14 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(
 // The tile loads are non-temporal: the streamed input would otherwise evict
 // the partly written scale lines (each 128-byte line of column-wise scales
 // collects 4 bytes from each of 32 tiles) before they are complete; measured
-// 5-7 % faster for both kernels.
+// 5-7 % faster for both kernels.  The bf16 quantize also stores its row- and
+// column-wise codes non-temporally, for the same reason: its tiles write as
+// many code bytes as they read, and through L2 they evicted the scale lines
+// between the tiles that share one, whose partial write-backs cost 12-17 % of
+// the kernel (measured by leaving the scale stores out).  Non-temporal code
+// stores gain almost all of it (11 % on 131072 x 7168, 18 % on the
+// 114688 x 4096 weight); the requantize, which reads a quarter as much, is
+// 10 % slower with them and keeps ordinary stores.
 //
 // LDS rows carry 16 bytes of padding after every 16 rows: the eight chunks j
 // of one read instruction (rows 16j + r) then start 4 banks apart, and the
@@ -188,7 +196,8 @@ __device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
 // same in lanes l and l ^ 1; the even lane stores it), s[c] the thread's sum
 // of column 4q + c over its 16 tokens (kDbias only: summed over the eight
 // chunks in a fixed butterfly order and stored as the tile's partial sum).
-template <bool kDbias>
+// kNT: the code stores are non-temporal (see quant_rowcol_kernel).
+template <bool kDbias, bool kNT = false>
 __device__ __forceinline__ void colwise_store(const uint32_t (&o)[4][4], const uint32_t (&x)[4],
                                               float (&s)[4], int64_t T, int64_t K, int64_t k0,
                                               int64_t t0, uint8_t* __restrict__ q_col,
@@ -199,9 +208,14 @@ __device__ __forceinline__ void colwise_store(const uint32_t (&o)[4][4], const u
   const uint32_t ts = (uint32_t)T, ss = (uint32_t)(T / 32);
   const uint32_t od = opaque_u32(4 * q * ts + 16 * j);
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<u32x4*>(q_col + (k0 * T + t0 + c * T) + od) =
-        u32x4{o[c][0], o[c][1], o[c][2], o[c][3]};
+  for (int c = 0; c < 4; ++c) {
+    u32x4* dst = reinterpret_cast<u32x4*>(q_col + (k0 * T + t0 + c * T) + od);
+    const u32x4 v = u32x4{o[c][0], o[c][1], o[c][2], o[c][3]};
+    if (kNT)
+      __builtin_nontemporal_store(v, dst);
+    else
+      *dst = v;
+  }
   // lane j holds block j / 2 of the quad's four columns (lanes 2i and 2i+1
   // agree); lane 0 of the quad gathers blocks 0..3 of each column (lanes 0,
   // 2, 4, 6) and stores them as one 32-bit word per column
@@ -252,6 +266,7 @@ __device__ __forceinline__ void load_bf16_tile(const uint16_t* __restrict__ x, i
 
 // Column-wise quantize of a staged 128 x 128 bf16 tile (columns k0.., tokens
 // t0..): thread -> column quad q = tid / 8, 16-token chunk j = tid % 8.
+template <bool kNT>
 __device__ __forceinline__ void colwise_pass_bf16(const uint8_t* lds, int64_t T, int64_t K,
                                                   int64_t k0, int64_t t0,
                                                   uint8_t* __restrict__ q_col,
@@ -295,7 +310,7 @@ __device__ __forceinline__ void colwise_pass_bf16(const uint8_t* lds, int64_t T,
                              __builtin_amdgcn_perm(hi[r + 3], hi[r + 2], 0x07060302u), sc[3]);
   }
   float unused[4] = {0.f, 0.f, 0.f, 0.f};
-  colwise_store<false>(o, xb, unused, T, K, k0, t0, q_col, s_col, nullptr);
+  colwise_store<false, kNT>(o, xb, unused, T, K, k0, t0, q_col, s_col, nullptr);
 }
 
 // Persistent: workgroup b takes tiles b, b + gridDim.x, ...; the loads of its
@@ -328,7 +343,8 @@ __global__ __launch_bounds__(kColThreads) void quant_rowcol_kernel(
         const uint32_t amax = quad_max(chunk_amax_bits(c));
         const uint32_t byte = scale_byte_from_exp(amax >> 7);
         const int64_t rb = t0 * K + k0 + 16 * jj * K;   // uniform
-        *reinterpret_cast<uint2*>(q_row + rb + ro) = encode_chunk(c, byte);
+        const uint2 e = encode_chunk(c, byte);
+        __builtin_nontemporal_store(u32x2{e.x, e.y}, reinterpret_cast<u32x2*>(q_row + rb + ro));
         // the 16 lanes of a row hold its 4 blocks: one 32-bit scale store
         const uint32_t bytes4 = gather_blocks4(byte);
         if ((tid & 15) == 0)
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(kColThreads) void quant_rowcol_kernel(
     const int next = tile + (int)gridDim.x;
     if (next < ntiles) load_bf16_tile(x, K, next, ntk, w);
 
-    colwise_pass_bf16(lds, T, K, k0, t0, q_col, s_col);
+    colwise_pass_bf16<true>(lds, T, K, k0, t0, q_col, s_col);
     if (next >= ntiles) break;
     __syncthreads();   // every column read of this tile is done before the next LDS write
     tile = next;
@@ -646,7 +662,6 @@ __global__ __launch_bounds__(256) void scaled_bias_partial_kernel(
     const int32_t* __restrict__ tile_expert, float* __restrict__ dbias_partial,
     float* __restrict__ dscale_partial) {
   __shared__ float red[4][8][64];
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 512 + 8 * lane;
   const int64_t t0 = (int64_t)blockIdx.y * kTileT + wave * 32;
@@ -940,7 +955,7 @@ __global__ __launch_bounds__(kColThreads) void swiglu_quant_kernel(
   }
   if (q_col == nullptr) return;
   __syncthreads();
-  colwise_pass_bf16(lds, T, F, k0, t0, q_col, s_col);
+  colwise_pass_bf16<false>(lds, T, F, k0, t0, q_col, s_col);
 }
 
 // ---------------------------------------------------------------------------

@@ -984,11 +984,13 @@ static int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-// Resident workgroups per CU of the persistent streaming kernels: quant_rowcol
-// is bound by LDS (35 KB per workgroup), requant by registers (up to 85 VGPRs:
-// five waves per SIMD).
+// Workgroups per CU of the persistent streaming kernels.  quant_rowcol is
+// bound by LDS (33 KB per workgroup: four).  requant could hold five (96
+// VGPRs) but runs 5 % faster with three: more resident tiles only add
+// concurrent pages and scale lines (five workgroups of quant_rowcol, with
+// the LDS padding replaced by a swizzle, were 1-5 % slower as well).
 constexpr int kRowcolWgPerCu = 4;
-constexpr int kRequantWgPerCu = 5;
+constexpr int kRequantWgPerCu = 3;
 
 hipError_t launch_quant_rowcol(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,

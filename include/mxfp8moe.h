@@ -205,6 +205,12 @@ mxfp8_status mxfp8_grouped_scaled_bias_grad(const uint8_t* q_row, const uint8_t*
  *  c_dtype: MXFP8_OUT_F32 or MXFP8_OUT_BF16 (round to nearest even).
  *  Rows of c that belong to no expert (none under the contract) are not
  *  written by NT/NN.
+ *  With fp32 output, an NT/NN call may split the few long tiles of its
+ *  grid's last round into two contraction halves: it then enqueues a small
+ *  kernel that zeroes those tiles' rows of c, and the two halves add into
+ *  them.  The result is deterministic (two fp32 adds onto zero commute) and
+ *  the launches stay stream-ordered and graph-capturable; their rounding
+ *  differs from the unsplit sum only by the order of the fp32 additions.
  * Errors: EINVAL for NULL pointers, bad layout, T % 128, N % 512, K % 512,
  * G < 1, host m_splits; ENOTSUP for another c_dtype.
  */

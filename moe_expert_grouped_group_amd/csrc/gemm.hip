@@ -78,6 +78,7 @@ struct GemmArgs {
   int32_t ntiles_n;                    // cols / BN
   int32_t band;                        // K-grouped: row tiles per expert (rows / BM)
   int32_t ntiles;                      // K-grouped: G * band * ntiles_n tiles
+  int32_t split_tail;                  // M-grouped, fp32 out: split the last round's tiles
 };
 
 // LDS layout of one stage: A tile [BM][BK], B tile [BN][BK]; 16-byte chunk c
@@ -275,6 +276,7 @@ struct TileDesc {
   int32_t row_hi;
   int32_t rows_avail;  // copied rows inside the operand (256, or T when T < 256)
   int32_t nblk;        // scale blocks of the tile's contraction (nk * 2)
+  int32_t split;       // one contraction half of a split tile: add into C atomically
 };
 
 template <bool KGROUPED>
@@ -353,6 +355,62 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
   d.row_lo = __builtin_amdgcn_readfirstlane(d.row_lo);
   d.row_hi = __builtin_amdgcn_readfirstlane(d.row_hi);
   d.rows_avail = __builtin_amdgcn_readfirstlane(d.rows_avail);
+  return d;
+}
+
+// Units of work of a launch.  Every unit is one tile, except in an M-grouped
+// launch with fp32 output whose last round of the grid would hold at most half
+// a grid of tiles: each of those `rem` tiles becomes two units, one per half
+// of its contraction, so the last round runs 2 rem half-length units instead
+// of rem whole tiles beside idle CUs (the dgrad of 8 experts 4096 -> 14336
+// has 1040 tiles: four full rounds on 256 CUs and 16 tiles in a fifth).  Both
+// halves add their partial products into C, zeroed beforehand by
+// zero_split_tail_kernel: (0 + a) + b and (0 + b) + a are the same fp32 sum,
+// so the result does not depend on which half lands first.
+// The split saves half a tile (nk / 2 MFMA steps) and costs the zeroing
+// launch and the atomic adds: measured about 32 steps plus 1.2 steps per split
+// tile (dgrad above, 224 steps and 16 tiles: 0.955 -> 0.905 ms; the forward of
+// the same workload, 64 steps and 56 tiles, was 7 % slower split), so a
+// launch splits only where nk / 2 exceeds that.
+struct UnitPlan {
+  int32_t nunits;
+  int32_t first_split;   // units from here on are contraction halves
+};
+
+__device__ __forceinline__ UnitPlan plan_units(const GemmArgs& p, int ntiles, int grid) {
+  UnitPlan u{ntiles, ntiles};
+  if (p.split_tail) {
+    const int rem = ntiles % grid;
+    const int nk = (int)(p.kc / KSTEP);
+    if (rem > 0 && 2 * rem <= grid && 5 * nk > 320 + 12 * rem) {
+      u.first_split = ntiles - rem;
+      u.nunits = ntiles + rem;
+    }
+  }
+  return u;
+}
+
+template <bool KGROUPED>
+__device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const ExpertTable* t,
+                                                  const UnitPlan& up, int unit, int64_t esz) {
+  if (KGROUPED || unit < up.first_split) {
+    TileDesc d = describe<KGROUPED>(p, t, unit, esz);
+    d.split = 0;
+    return d;
+  }
+  const int v = unit - up.first_split;
+  const int half = v & 1;
+  TileDesc d = describe<KGROUPED>(p, t, up.first_split + (v >> 1), esz);
+  // contraction bytes [half kc/2, (half + 1) kc/2) of the tile (kc % 1024 == 0:
+  // each half is a whole number of stages and of 8-step scale groups)
+  const int64_t hk = half * (p.kc / 2);
+  d.a = uniform_ptr(d.a + hk);
+  d.b = uniform_ptr(d.b + hk);
+  d.sa = uniform_ptr(d.sa + hk / 32);
+  d.sb = uniform_ptr(d.sb + hk / 32);
+  d.nk >>= 1;
+  d.nblk >>= 1;
+  d.split = 1;
   return d;
 }
 
@@ -514,9 +572,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  int tile = blockIdx.x;
-  if (tile >= ntiles) return;
-  TileDesc cur = describe<KGROUPED>(p, &table, tile, esz);
+  const UnitPlan up = plan_units(p, ntiles, (int)gridDim.x);
+  int tile = blockIdx.x;   // unit index (a tile, or half of one: describe_unit)
+  if (tile >= up.nunits) return;
+  TileDesc cur = describe_unit<KGROUPED>(p, &table, up, tile, esz);
   setup(cur);
   tile_prologue(cur.nk);
 
@@ -665,8 +724,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     const int next = tile + gridDim.x;
     TileDesc nxt;
     nxt.nk = 0;
-    if (next < ntiles) {
-      nxt = describe<KGROUPED>(p, &table, next, esz);
+    if (next < up.nunits) {
+      nxt = describe_unit<KGROUPED>(p, &table, up, next, esz);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
       setup(nxt);
@@ -677,7 +736,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // expert table (LDS) rather than kept from the tile start: held across
     // the K loop they are spilled, and the reload's wait on the vector memory
     // counter would also wait for the next tile's copies issued above.
-    const TileDesc ed = describe<KGROUPED>(p, &table, tile, esz);
+    const TileDesc ed = describe_unit<KGROUPED>(p, &table, up, tile, esz);
 
     // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
     // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32.
@@ -698,22 +757,40 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (int64_t)(wn * WT + fr) * esz);
       const int lo = ed.row_lo, hi = ed.row_hi;
       const bool part = lo > 0 || hi < BM;
+      // a contraction half of a split tile adds into C (branch outside the
+      // store loop, which stays as it is for whole tiles)
+      if (!OUT_BF16 && ed.split) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
-          if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
-          char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+            if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
+            char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (OUT_BF16)
-              __builtin_nontemporal_store(
-                  (uint16_t)f32_to_bf16(acc[i][j][r]),
-                  (__attribute__((address_space(1))) uint16_t*)(rbase + j * 32 * 2));
-            else
-              __builtin_nontemporal_store(
-                  acc[i][j][r], (__attribute__((address_space(1))) float*)(rbase + j * 32 * 4));
+            for (int j = 0; j < 4; ++j)
+              (void)__builtin_amdgcn_global_atomic_fadd_f32(
+                  (__attribute__((address_space(1))) float*)(rbase + j * 32 * 4), acc[i][j][r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+            if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
+            char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (OUT_BF16)
+                __builtin_nontemporal_store(
+                    (uint16_t)f32_to_bf16(acc[i][j][r]),
+                    (__attribute__((address_space(1))) uint16_t*)(rbase + j * 32 * 2));
+              else
+                __builtin_nontemporal_store(
+                    acc[i][j][r], (__attribute__((address_space(1))) float*)(rbase + j * 32 * 4));
+            }
           }
         }
       }
@@ -795,9 +872,31 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         }
       }
     }
-    if (next >= ntiles) break;
+    if (next >= up.nunits) break;
     tile = next;
     cur = nxt;
+  }
+}
+
+// Zeroes the output rows of the tiles that describe_unit splits in two (the
+// same plan, from the same device m_splits and grid), before the GEMM adds
+// both halves into them.  fp32 output only.
+__global__ __launch_bounds__(kThreads) void zero_split_tail_kernel(GemmArgs p, int32_t grid) {
+  __shared__ ExpertTable table;
+  __shared__ int64_t scan[2 * kThreads];
+  build_table<false>(p.m_splits, p.G, &table, scan);
+  const int ntiles = table.tpre[p.G] * p.ntiles_n;
+  const UnitPlan up = plan_units(p, ntiles, grid);
+  const int rem = up.nunits - ntiles;
+  for (int b = blockIdx.x; b < rem; b += gridDim.x) {
+    const TileDesc d = describe<false>(p, &table, up.first_split + b, 4);
+    float* c = reinterpret_cast<float*>(d.c);
+    const int rows = d.row_hi - d.row_lo;
+    for (int idx = threadIdx.x; idx < rows * (BN / 4); idx += kThreads) {
+      const int r = d.row_lo + idx / (BN / 4);
+      *reinterpret_cast<float4*>(c + (int64_t)r * p.ldc + 4 * (idx % (BN / 4))) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 }
 
@@ -853,6 +952,15 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+  // contraction halves of the last round's tiles (describe_unit): fp32
+  // output, M-grouped, and halves that are whole stages and scale groups
+  p.split_tail = (!kgrouped && !out_bf16 && p.kc % 1024 == 0) ? 1 : 0;
+  if (p.split_tail) {
+    hipLaunchKernelGGL(zero_split_tail_kernel, dim3(std::max(1u, grid / 2)), dim3(kThreads), 0,
+                       st, p, (int32_t)grid);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (kgrouped && accumulate) return launch_one<true, false, true>(p, grid, st);
   if (kgrouped)
     return out_bf16 ? launch_one<true, true>(p, grid, st) : launch_one<true, false>(p, grid, st);

@@ -106,6 +106,47 @@ def test_three_layouts_synthetic(kind, case, out_dtype):
 
 
 @pytest.mark.parametrize("kind", ["random", "integer"])
+@pytest.mark.parametrize("layout", ["NT", "NN"])
+def test_split_contraction_halves(kind, layout):
+    """Forward and dgrad launches whose last round holds few, long tiles split
+    each of those tiles into two contraction halves added into a zeroed C
+    (fp32 output).  Here every tile is split: 384 tokens as [256, 128, 0, 0]
+    (a full tile, and a 128-row tile of the second expert whose copied rows
+    are shifted back to stay inside the operand), 5120-long contractions, 512
+    outputs, a grid of
+    10 workgroups for 4 tiles.  The output buffer starts as garbage: the split
+    tiles must be cleared before their halves are added."""
+    splits = [256, 128, 0, 0]
+    g, t = len(splits), sum(splits)
+    kc, other = 5120, 512
+    rng = np.random.default_rng(77 if kind == "random" else 78)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    if layout == "NT":
+        n, k = other, kc
+        aq, as_ = _mx_rows(rng, t, k, kind)
+        bq, bs = _mx_rows(rng, g * n, k, kind)
+        ref, mag, win = og.fprop(aq, as_, bq.reshape(g, n, k), bs.reshape(g, n, k // 32), splits,
+                                 True, True)
+        shape = (t, n)
+    else:
+        n, k = kc, other
+        aq, as_ = _mx_rows(rng, t, n, kind)
+        bq, bs = _mx_rows(rng, k, g * n, kind)
+        ref, mag, win = og.dgrad(aq, as_, bq, bs, splits, g, True, True)
+        shape = (t, k)
+    for rep in range(2):
+        out = torch.full(shape, 7.0 + rep, dtype=torch.float32, device="cuda")
+        log(f"gemm {layout} split halves {kind} call {rep}")
+        mx.grouped_gemm(layout, dev(aq), dev(as_), dev(bq), dev(bs), ms, t, n, k, torch.float32,
+                        out)
+        torch.cuda.synchronize()
+        if kind == "integer":
+            assert np.array_equal(f64(out), ref)
+        else:
+            _check(f64(out), ref, mag, torch.float32, win)
+
+
+@pytest.mark.parametrize("kind", ["random", "integer"])
 @pytest.mark.parametrize("case", [0, 2, 4])
 def test_wgrad_accumulate(kind, case):
     """main_grad[g] += dY_g^T X_g in place.  Bound: the wgrad bound of the

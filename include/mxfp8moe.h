@@ -45,6 +45,11 @@
  *    `stream` (a hipStream_t; NULL = the default stream), so the calls can
  *    be captured in a HIP graph.  Kernels never fill memory with a memset
  *    node.
+ *  - T = 0 (no token routed to any expert) is valid everywhere: the buffers
+ *    whose size is a multiple of T are empty and may be NULL; outputs that
+ *    do not depend on T (the wgrad's [G, N, K], dbias [G, N]) must still be
+ *    given and are written as for experts without tokens (zeros), and an
+ *    accumulated main_grad is left as it is.
  *  - Errors: the return value is a status code; mxfp8_last_error() gives a
  *    message for the last failing call on this thread.  MXFP8_EINVAL mirrors
  *    the pages' ValueError (bad shapes, NULL pointers, host m_splits),

@@ -78,16 +78,16 @@ mxfp8_status mxfp8_group_quantize(const uint16_t* x, int64_t T, int64_t K, uint3
                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                                   uint8_t* s_col, const int32_t* noop_flag, void* stream) {
   const char* fn = "mxfp8_group_quantize";
-  REQUIRE(x != nullptr, "%s: x is NULL", fn);
+  REQUIRE(x != nullptr || T == 0, "%s: x is NULL", fn);
   REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
           "%s: usage must be a non-empty combination of MXFP8_ROWWISE and MXFP8_COLWISE", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
           (long long)K);
+  if (T == 0) return ok();   // nothing to read or write: every buffer is empty
   const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
   REQUIRE(!row || (q_row && s_row), "%s: ROWWISE requested but q_row/s_row is NULL", fn);
   REQUIRE(!col || (q_col && s_col), "%s: COLWISE requested but q_col/s_col is NULL", fn);
-  if (T == 0) return ok();
   hipError_t e;
   if (col)
     e = mx::launch_quant_rowcol(x, T, K, row ? q_row : nullptr, row ? s_row : nullptr, q_col,
@@ -102,7 +102,7 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
                                    const int64_t* m_splits, int32_t G, float* dbias,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "mxfp8_requant_colwise";
-  REQUIRE(q_row && s_row && q_col && s_col, "%s: NULL data/scale pointer", fn);
+  REQUIRE(T == 0 || (q_row && s_row && q_col && s_col), "%s: NULL data/scale pointer", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
           (long long)K);
@@ -110,7 +110,8 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
   if (dbias != nullptr) {
     mxfp8_status st = check_device_splits(m_splits, G, fn);
     if (st != MXFP8_OK) return st;
-    REQUIRE(workspace != nullptr && workspace_bytes >= mxfp8_dbias_workspace_bytes(T, K),
+    REQUIRE((workspace != nullptr || T == 0) &&
+                workspace_bytes >= mxfp8_dbias_workspace_bytes(T, K),
             "%s: dbias needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, K));
     partial = static_cast<float*>(workspace);
   }
@@ -126,13 +127,14 @@ mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int
                                  int64_t N, const int64_t* m_splits, int32_t G, float* dbias,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "mxfp8_grouped_dbias";
-  REQUIRE(q_row && s_row && dbias, "%s: NULL pointer", fn);
+  REQUIRE(dbias && (T == 0 || (q_row && s_row)), "%s: NULL pointer", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
           (long long)N);
   mxfp8_status s = check_device_splits(m_splits, G, fn);
   if (s != MXFP8_OK) return s;
-  REQUIRE(workspace != nullptr && workspace_bytes >= mxfp8_dbias_workspace_bytes(T, N),
+  REQUIRE((workspace != nullptr || T == 0) &&
+              workspace_bytes >= mxfp8_dbias_workspace_bytes(T, N),
           "%s: needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, N));
   float* partial = static_cast<float*>(workspace);
   hipStream_t st = as_stream(stream);
@@ -153,10 +155,10 @@ mxfp8_status mxfp8_grouped_scaled_bias_grad(const uint8_t* q_row, const uint8_t*
                                             float* dbias, float* dscales, void* workspace,
                                             size_t workspace_bytes, void* stream) {
   const char* fn = "mxfp8_grouped_scaled_bias_grad";
-  REQUIRE(q_row && s_row, "%s: NULL data/scale pointer", fn);
+  REQUIRE(T == 0 || (q_row && s_row), "%s: NULL data/scale pointer", fn);
   REQUIRE(dbias || dscales, "%s: neither dbias nor dscales requested", fn);
-  REQUIRE(!dbias || scales, "%s: dbias needs the routing scales", fn);
-  REQUIRE(!dscales || bias, "%s: dscales needs the bias", fn);
+  REQUIRE(!dbias || scales || T == 0, "%s: dbias needs the routing scales", fn);
+  REQUIRE(!dscales || bias || T == 0, "%s: dscales needs the bias", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
           (long long)N);
@@ -186,7 +188,10 @@ mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uin
   if (c_dtype != MXFP8_OUT_F32 && c_dtype != MXFP8_OUT_BF16)
     return fail(MXFP8_ENOTSUP, "%s: output dtype %d is not supported (f32 = 0, bf16 = 1)", fn,
                 (int)c_dtype);
-  REQUIRE(a_data && a_scale && b_data && b_scale && c, "%s: NULL operand pointer", fn);
+  // with no tokens nothing is read, and the forward/dgrad output is empty too
+  REQUIRE(T == 0 || (a_data && a_scale && b_data && b_scale && c), "%s: NULL operand pointer",
+          fn);
+  REQUIRE(c || layout != MXFP8_LAYOUT_TN, "%s: NULL output", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
           (long long)N);
@@ -208,7 +213,8 @@ mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const ui
                                                  const int64_t* m_splits, int32_t G,
                                                  void* stream) {
   const char* fn = "mxfp8_grouped_gemm_wgrad_accumulate";
-  REQUIRE(a_data && a_scale && b_data && b_scale && main_grad, "%s: NULL pointer", fn);
+  REQUIRE(main_grad && (T == 0 || (a_data && a_scale && b_data && b_scale)), "%s: NULL pointer",
+          fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(N > 0 && N % 512 == 0, "%s: N = %lld must be a positive multiple of 512", fn,
           (long long)N);
@@ -237,7 +243,7 @@ mxfp8_status mxfp8_validate_splits(const int64_t* m_splits, int32_t G, int64_t T
 mxfp8_status mxfp8_swiglu_fwd(const uint16_t* h, int64_t T, int64_t F, uint16_t* a,
                               void* stream) {
   const char* fn = "mxfp8_swiglu_fwd";
-  REQUIRE(h && a, "%s: NULL pointer", fn);
+  REQUIRE(T == 0 || (h && a), "%s: NULL pointer", fn);
   REQUIRE(T >= 0, "%s: T < 0", fn);
   REQUIRE(F > 0 && F % 8 == 0, "%s: F = %lld must be a positive multiple of 8", fn, (long long)F);
   if (T == 0) return ok();
@@ -248,16 +254,16 @@ mxfp8_status mxfp8_swiglu_quantize(const uint16_t* h, int64_t T, int64_t F, uint
                                    uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                                    uint8_t* s_col, void* stream) {
   const char* fn = "mxfp8_swiglu_quantize";
-  REQUIRE(h != nullptr, "%s: h is NULL", fn);
+  REQUIRE(h != nullptr || T == 0, "%s: h is NULL", fn);
   REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
           "%s: usage must be a non-empty combination of MXFP8_ROWWISE and MXFP8_COLWISE", fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
   REQUIRE(F > 0 && F % 512 == 0, "%s: F = %lld must be a positive multiple of 512", fn,
           (long long)F);
+  if (T == 0) return ok();   // nothing to read or write: every buffer is empty
   const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
   REQUIRE(!row || (q_row && s_row), "%s: ROWWISE requested but q_row/s_row is NULL", fn);
   REQUIRE(!col || (q_col && s_col), "%s: COLWISE requested but q_col/s_col is NULL", fn);
-  if (T == 0) return ok();
   return hip_status(mx::launch_swiglu_quant(h, T, F, row ? q_row : nullptr, row ? s_row : nullptr,
                                             col ? q_col : nullptr, col ? s_col : nullptr,
                                             as_stream(stream)),
@@ -267,7 +273,7 @@ mxfp8_status mxfp8_swiglu_quantize(const uint16_t* h, int64_t T, int64_t F, uint
 mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                               uint16_t* dh, void* stream) {
   const char* fn = "mxfp8_swiglu_bwd";
-  REQUIRE(h && da && dh, "%s: NULL pointer", fn);
+  REQUIRE(T == 0 || (h && da && dh), "%s: NULL pointer", fn);
   REQUIRE(T >= 0, "%s: T < 0", fn);
   REQUIRE(F > 0 && F % 8 == 0, "%s: F = %lld must be a positive multiple of 8", fn, (long long)F);
   if (T == 0) return ok();

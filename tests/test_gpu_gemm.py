@@ -113,8 +113,8 @@ def test_split_contraction_halves(kind, layout):
     (fp32 output).  Here every tile is split: 384 tokens as [256, 128, 0, 0]
     (a full tile, and a 128-row tile of the second expert whose copied rows
     are shifted back to stay inside the operand), 5120-long contractions, 512
-    outputs, a grid of
-    10 workgroups for 4 tiles.  The output buffer starts as garbage: the split
+    outputs, a grid of 10 workgroups for 4 tiles.  The output buffer starts as
+    garbage: the split
     tiles must be cleared before their halves are added."""
     splits = [256, 128, 0, 0]
     g, t = len(splits), sum(splits)

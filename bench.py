@@ -15,7 +15,10 @@ tokens routed by a seeded Dirichlet(1) multinomial (multiples of 128); X, dY
 HBM before the timed region.
 
 value = 3 * 2 T N K / step time (TFLOP/s over the whole step, quantize
-kernels included).  The grouped-GEMM roofline uses the GEMM launches' own
+kernels included).  The timed steps run twice: as eager launches, each
+bracketed by events (the per-launch times in kernel_ms, and
+ms_per_step_eager), then replayed from a HIP graph of the same launches
+(ms_per_step and value; --eager keeps the eager figure).  The grouped-GEMM roofline uses the GEMM launches' own
 durations, measured with events on the stream they run on.
 
 HBM traffic of the GEMM launches (roofline "traffic") comes from the FETCH_SIZE
@@ -60,6 +63,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as eager launches only (no graph replay)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads (skewed 128-expert linear, fused MLP, "
                          "standalone group quantize)")
@@ -422,6 +427,20 @@ def main():
         ev.setdefault(name, []).append((a, b))
         return r
 
+    def step_plain():
+        mx.group_quantize(x, mx.ROWWISE, out=xo)
+        mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo)
+        mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
+                        out_dtype, y)
+        mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)
+        mx.group_quantize(dy, mx.ROWWISE, out=dyo)
+        mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n, k,
+                        out_dtype, dx)
+        mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db,
+                           workspace=ws)
+        mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k,
+                        out_dtype, dw)
+
     def step():
         timed("quant_x", lambda: mx.group_quantize(x, mx.ROWWISE, out=xo))
         timed("quant_w", lambda: mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo))
@@ -453,8 +472,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / args.steps
+    ms_step_eager = ms_step
 
     per = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
+
+    if not args.eager:
+        # The timed steps again, replayed from a HIP graph of the same eight
+        # launches (captured once; every output buffer is caller-owned, so a
+        # replay rewrites the same memory): no host launch gaps between the
+        # kernels.  The per-launch times above come from the eager steps.
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step_plain()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                step_plain()
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = start.elapsed_time(stop) / args.steps
 
     # Outside the step: wgrad accumulated into an fp32 main_grad (the
     # production form of the wgrad launch), timed on the same operands.
@@ -519,6 +565,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -954,7 +954,10 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
   // contraction halves of the last round's tiles (describe_unit): fp32
   // output, M-grouped, and halves that are whole stages and scale groups
-  p.split_tail = (!kgrouped && !out_bf16 && p.kc % 1024 == 0) ? 1 : 0;
+  // (and only where the contraction is long enough to split one tile:
+  // plan_units with rem = 1; otherwise the zeroing launch is left out)
+  p.split_tail = (!kgrouped && !out_bf16 && p.kc % 1024 == 0 &&
+                  5 * (p.kc / KSTEP) > 320 + 12) ? 1 : 0;
   if (p.split_tail) {
     hipLaunchKernelGGL(zero_split_tail_kernel, dim3(std::max(1u, grid / 2)), dim3(kThreads), 0,
                        st, p, (int32_t)grid);

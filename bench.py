@@ -31,7 +31,9 @@ same way (fewer steps) and reported under "other_workloads": the skewed
 128-expert linear (hidden 7168 -> 2048, 38 experts without tokens), the fused
 expert MLP forward and backward (64 experts, 83968 tokens, 3072 -> 2048 ->
 SwiGLU -> 1024 -> 3072, bf16 outputs) and the standalone row + column-wise
-group quantize of 131072 x 7168.
+group quantize of 131072 x 7168.  Every wgrad launch passes a tile-counter
+workspace (mxfp8_grouped_gemm_ws), with which the kernel hands out the wgrad
+tiles dynamically unless 1 expert in 8 or more has no token.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
        python bench.py --calibrate-copy      (copy of 1 GiB, for counter scaling)
@@ -241,6 +243,7 @@ def bench_skewed_linear(steps, warmup):
     dx = torch.empty(t, k, dtype=f32, device="cuda")
     dw = torch.empty(g, n, k, dtype=f32, device="cuda")
     ws = torch.empty(mx.dbias_workspace_bytes(t, n), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
     launches = [
         ("quant_w", lambda: mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo)),
         ("gemm_fprop", lambda: mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data,
@@ -253,7 +256,8 @@ def bench_skewed_linear(steps, warmup):
                                                         with_dbias=True, out=dyc, dbias=db,
                                                         workspace=ws)),
         ("gemm_wgrad", lambda: mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data,
-                                               xc.col_scale, ms, t, n, k, f32, dw)),
+                                               xc.col_scale, ms, t, n, k, f32, dw,
+                                               workspace=gws)),
     ]
     ms_step, per = _run_steps(launches, steps, warmup)
     flop = 2.0 * t * n * k
@@ -313,6 +317,7 @@ def bench_fused_mlp(steps, warmup):
     dx = torch.empty(t, k, dtype=bf, device="cuda")
     dw1 = torch.empty(g, n2, k, dtype=bf, device="cuda")
     ws = torch.empty(mx.dbias_workspace_bytes(t, n2), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
     gemm = mx.grouped_gemm
     launches = [
         ("quant_x", lambda: mx.group_quantize(x, R, out=xo)),
@@ -329,7 +334,7 @@ def bench_fused_mlp(steps, warmup):
                                    w2o.col_scale, ms, t, k, f, bf, da)),
         ("requant_dy", lambda: mx.requant_colwise(dyo.row_data, dyo.row_scale, out=dyc)),
         ("fc2_wgrad", lambda: gemm("TN", dyc.col_data, dyc.col_scale, ao.col_data, ao.col_scale,
-                                   ms, t, k, f, bf, dw2)),
+                                   ms, t, k, f, bf, dw2, workspace=gws)),
         ("swiglu_bwd", lambda: mx.swiglu_bwd(h, da, out=dh)),
         ("quant_dh", lambda: mx.group_quantize(dh, R, out=dho)),
         ("fc1_dgrad", lambda: gemm("NN", dho.row_data, dho.row_scale, w1o.col_data,
@@ -338,7 +343,7 @@ def bench_fused_mlp(steps, warmup):
                                                         with_dbias=True, out=dhc, dbias=db1,
                                                         workspace=ws)),
         ("fc1_wgrad", lambda: gemm("TN", dhc.col_data, dhc.col_scale, xc.col_data, xc.col_scale,
-                                   ms, t, n2, k, bf, dw1)),
+                                   ms, t, n2, k, bf, dw1, workspace=gws)),
     ]
     ms_step, per = _run_steps(launches, steps, warmup)
     flops = 3 * 2.0 * t * k * n2 + 3 * 2.0 * t * f * k
@@ -415,6 +420,7 @@ def main():
     dw = torch.empty(g, n, k, dtype=out_dtype, device=dev)
     db = torch.empty(g, n, dtype=torch.float32, device=dev)
     ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8)
+    gws = torch.empty(mx.gemm_workspace_bytes(), **u8)   # wgrad tile counter
 
     ev = {}
 
@@ -439,7 +445,7 @@ def main():
         mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db,
                            workspace=ws)
         mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k,
-                        out_dtype, dw)
+                        out_dtype, dw, workspace=gws)
 
     def step():
         timed("quant_x", lambda: mx.group_quantize(x, mx.ROWWISE, out=xo))
@@ -455,7 +461,7 @@ def main():
             dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db, workspace=ws))
         timed("gemm_wgrad", lambda: mx.grouped_gemm(
             "TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, out_dtype,
-            dw))
+            dw, workspace=gws))
 
     for _ in range(args.warmup):
         step()
@@ -508,7 +514,8 @@ def main():
     if out_dtype == torch.float32:
         main_grad = torch.zeros(g, n, k, dtype=torch.float32, device=dev)
         acc = lambda: mx.grouped_gemm_wgrad_accumulate(  # noqa: E731
-            dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, main_grad)
+            dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, main_grad,
+            workspace=gws)
         acc_ms = _time_outside(acc, args.steps)
         del main_grad
 

@@ -246,6 +246,43 @@ mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const ui
                                                  void* stream);
 
 /*
+ * mxfp8_grouped_gemm_ws, mxfp8_grouped_gemm_wgrad_accumulate_ws -- the same
+ * calls with a caller-owned device workspace holding a tile counter, through
+ * which the TN (wgrad) tiles are handed out in order as workgroups finish
+ * theirs: greedy longest-first placement of the experts' tiles, instead of a
+ * fixed assignment that, under skewed routing, lets a few workgroups with the
+ * largest experts' tiles run long after the rest (the routing skew of the
+ * [P3224] m_splits use case; [P3545]'s fused grouped MLP).  The outputs are
+ * bit-identical to those of the calls without a workspace (each tile is
+ * computed the same way, by whichever workgroup takes it).  NT/NN ignore the
+ * workspace.
+ *  The kernel keeps the fixed order when 1 expert in 8 or more has no token:
+ *  those experts' tiles store zeros only, and the fixed order runs them
+ *  beside the contraction instead of last.
+ *  workspace: device memory of at least mxfp8_grouped_gemm_workspace_bytes()
+ *  bytes, owned by the caller; its contents need no initialisation (the call
+ *  enqueues a one-thread kernel that sets the counter before the GEMM) and
+ *  are meaningless afterwards.  Calls that may run at the same time (other
+ *  streams) need workspaces of their own; stream-ordered calls, graph replays
+ *  included, can share one.
+ * Errors: as the calls without a workspace, and EINVAL for a NULL or too
+ * small workspace.
+ */
+size_t mxfp8_grouped_gemm_workspace_bytes(void);
+mxfp8_status mxfp8_grouped_gemm_ws(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
+                                   const uint8_t* b_data, const uint8_t* b_scale, void* c,
+                                   int32_t c_dtype, int64_t T, int64_t N, int64_t K,
+                                   const int64_t* m_splits, int32_t G, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate_ws(const uint8_t* a_data,
+                                                    const uint8_t* a_scale, const uint8_t* b_data,
+                                                    const uint8_t* b_scale, float* main_grad,
+                                                    int64_t T, int64_t N, int64_t K,
+                                                    const int64_t* m_splits, int32_t G,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    void* stream);
+
+/*
  * mxfp8_validate_splits -- device-side check of the alignment contract on the
  * device splits ([P3224] review: an alignment check must accompany device
  * m_splits).  Writes *flag (device int32) = bitmask: 1 = a negative split,

@@ -35,6 +35,11 @@ SIGNATURES = {
     "mxfp8_validate_splits": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp]),
     "mxfp8_grouped_gemm_wgrad_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
                                                     c_i64, c_vp, c_i32, c_vp]),
+    "mxfp8_grouped_gemm_workspace_bytes": (c_size, []),
+    "mxfp8_grouped_gemm_ws": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64,
+                                      c_i64, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "mxfp8_grouped_gemm_wgrad_accumulate_ws": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                       c_i64, c_vp, c_i32, c_vp, c_size, c_vp]),
     "mxfp8_swiglu_fwd": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "mxfp8_swiglu_bwd": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "mxfp8_swiglu_quantize": (c_i32, [c_vp, c_i64, c_i64, c_u32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -45,7 +50,7 @@ SIGNATURES = {
     "mxfp8_convert_sweep": (c_i32, [c_i32, c_vp, c_size, c_vp]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 MXFP8_OK, MXFP8_EINVAL, MXFP8_ENOTSUP, MXFP8_EHIP = 0, 1, 2, 3
 

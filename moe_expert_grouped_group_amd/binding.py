@@ -245,13 +245,27 @@ def grouped_scaled_bias_grad(row_data, row_scale, m_splits, scales=None, bias=No
     return dbias, dscales
 
 
+def gemm_workspace_bytes():
+    return int(_lib().mxfp8_grouped_gemm_workspace_bytes())
+
+
+def _gemm_workspace(workspace):
+    need = gemm_workspace_bytes()
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device buffer of at least {need} bytes")
+    return workspace
+
+
 def grouped_gemm(layout, a_data, a_scale, b_data, b_scale, m_splits, tokens, n, k,
-                 out_dtype=torch.float32, out=None, stream=None):
+                 out_dtype=torch.float32, out=None, stream=None, workspace=None):
     """One grouped GEMM of an expert linear (in_features k, out_features n).
 
     layout "NT" (forward): a = X row-wise [T, k], b = W row-wise [G, n, k] -> [T, n]
     layout "NN" (dgrad):   a = dY row-wise [T, n], b = W column-wise [k, G*n] -> [T, k]
     layout "TN" (wgrad):   a = dY column-wise [n, T], b = X column-wise [k, T] -> [G, n, k]
+
+    workspace: optional device buffer of gemm_workspace_bytes(); with it the
+    wgrad tiles are handed out dynamically (mxfp8_grouped_gemm_ws), same bytes.
     """
     lib = _lib()
     lay = _LAYOUTS[layout]
@@ -273,14 +287,21 @@ def grouped_gemm(layout, a_data, a_scale, b_data, b_scale, m_splits, tokens, n, 
     if out is None:
         out = _empty(shapes[4], out_dtype, a2)
     _need(out, out_dtype, shapes[4], "out")
-    st = lib.mxfp8_grouped_gemm(lay, _ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2), _ptr(out),
-                                _OUT[out_dtype], t, n, k, _ptr(ms), g, _stream(stream))
-    _native.check(st, "mxfp8_grouped_gemm")
+    if workspace is None:
+        st = lib.mxfp8_grouped_gemm(lay, _ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2), _ptr(out),
+                                    _OUT[out_dtype], t, n, k, _ptr(ms), g, _stream(stream))
+        _native.check(st, "mxfp8_grouped_gemm")
+    else:
+        ws = _gemm_workspace(workspace)
+        st = lib.mxfp8_grouped_gemm_ws(lay, _ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2), _ptr(out),
+                                       _OUT[out_dtype], t, n, k, _ptr(ms), g, _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream))
+        _native.check(st, "mxfp8_grouped_gemm_ws")
     return out
 
 
 def grouped_gemm_wgrad_accumulate(a_data, a_scale, b_data, b_scale, m_splits, tokens, n, k,
-                                  main_grad, stream=None):
+                                  main_grad, stream=None, workspace=None):
     """wgrad added into an fp32 main_grad [G, n, k] in place:
     main_grad[g] += dY_g^T X_g (a = dY column-wise [n, T], b = X column-wise
     [k, T]); experts without tokens keep their main_grad untouched."""
@@ -293,10 +314,17 @@ def grouped_gemm_wgrad_accumulate(a_data, a_scale, b_data, b_scale, m_splits, to
     b2 = _as_shape(b_data, (k, t), "b_data")
     bs2 = _as_shape(b_scale, (k, t // 32), "b_scale")
     _need(main_grad, torch.float32, (g, n, k), "main_grad")
-    st = lib.mxfp8_grouped_gemm_wgrad_accumulate(_ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2),
-                                                 _ptr(main_grad), t, n, k, _ptr(ms), g,
-                                                 _stream(stream))
-    _native.check(st, "mxfp8_grouped_gemm_wgrad_accumulate")
+    if workspace is None:
+        st = lib.mxfp8_grouped_gemm_wgrad_accumulate(_ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2),
+                                                     _ptr(main_grad), t, n, k, _ptr(ms), g,
+                                                     _stream(stream))
+        _native.check(st, "mxfp8_grouped_gemm_wgrad_accumulate")
+    else:
+        ws = _gemm_workspace(workspace)
+        st = lib.mxfp8_grouped_gemm_wgrad_accumulate_ws(
+            _ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2), _ptr(main_grad), t, n, k, _ptr(ms), g,
+            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _native.check(st, "mxfp8_grouped_gemm_wgrad_accumulate_ws")
     return main_grad
 
 

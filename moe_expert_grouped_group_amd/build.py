@@ -5,7 +5,7 @@
 Each source is compiled by hipcc into an object under ``_build/`` (in
 parallel), then linked into ``moe_expert_grouped_group_amd/libmxfp8moe.so``.
 Packed-fp32 instructions are disabled for the device code
-(``-target-feature -packed-fp32-ops``).
+(``-target-feature -packed-fp32-ops``), and so is the atomic optimizer.
 """
 
 import os
@@ -33,6 +33,10 @@ def _hipcc():
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # atomics stay single instructions: the atomic optimizer would
+            # turn the GEMM's tile-counter fetch into a wave-wide form that
+            # waits for every outstanding memory operation right after it
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-Wno-unused-command-line-argument", "-Wno-inline-asm",
             "-I", os.path.join(ROOT, "include")]
 

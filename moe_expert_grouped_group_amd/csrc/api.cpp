@@ -67,7 +67,7 @@ extern "C" {
 
 const char* mxfp8_last_error(void) { return g_err; }
 
-int32_t mxfp8_abi_version(void) { return 2; }
+int32_t mxfp8_abi_version(void) { return 3; }
 
 size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0) return 0;
@@ -178,11 +178,11 @@ mxfp8_status mxfp8_grouped_scaled_bias_grad(const uint8_t* q_row, const uint8_t*
                     fn);
 }
 
-mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
-                                const uint8_t* b_data, const uint8_t* b_scale, void* c,
-                                int32_t c_dtype, int64_t T, int64_t N, int64_t K,
-                                const int64_t* m_splits, int32_t G, void* stream) {
-  const char* fn = "mxfp8_grouped_gemm";
+static mxfp8_status grouped_gemm_impl(const char* fn, int32_t layout, const uint8_t* a_data,
+                                      const uint8_t* a_scale, const uint8_t* b_data,
+                                      const uint8_t* b_scale, void* c, int32_t c_dtype, int64_t T,
+                                      int64_t N, int64_t K, const int64_t* m_splits, int32_t G,
+                                      int32_t* queue, void* stream) {
   REQUIRE(layout == MXFP8_LAYOUT_NT || layout == MXFP8_LAYOUT_NN || layout == MXFP8_LAYOUT_TN,
           "%s: layout %d is not NT(0), NN(1) or TN(2)", fn, (int)layout);
   if (c_dtype != MXFP8_OUT_F32 && c_dtype != MXFP8_OUT_BF16)
@@ -203,16 +203,15 @@ mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uin
   if (T == 0 && layout != MXFP8_LAYOUT_TN) return ok();
   const hipError_t e = mx::launch_grouped_gemm(layout, a_data, a_scale, b_data, b_scale, c,
                                                c_dtype == MXFP8_OUT_BF16, T, N, K, m_splits, G,
-                                               false, as_stream(stream));
+                                               false, as_stream(stream), queue);
   return hip_status(e, fn);
 }
 
-mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const uint8_t* a_scale,
-                                                 const uint8_t* b_data, const uint8_t* b_scale,
-                                                 float* main_grad, int64_t T, int64_t N, int64_t K,
-                                                 const int64_t* m_splits, int32_t G,
-                                                 void* stream) {
-  const char* fn = "mxfp8_grouped_gemm_wgrad_accumulate";
+static mxfp8_status wgrad_accumulate_impl(const char* fn, const uint8_t* a_data,
+                                          const uint8_t* a_scale, const uint8_t* b_data,
+                                          const uint8_t* b_scale, float* main_grad, int64_t T,
+                                          int64_t N, int64_t K, const int64_t* m_splits,
+                                          int32_t G, int32_t* queue, void* stream) {
   REQUIRE(main_grad && (T == 0 || (a_data && a_scale && b_data && b_scale)), "%s: NULL pointer",
           fn);
   REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
@@ -226,8 +225,60 @@ mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const ui
   if (T == 0) return ok();   // every expert is empty: main_grad stays as it is
   const hipError_t e =
       mx::launch_grouped_gemm(MXFP8_LAYOUT_TN, a_data, a_scale, b_data, b_scale, main_grad, false,
-                              T, N, K, m_splits, G, true, as_stream(stream));
+                              T, N, K, m_splits, G, true, as_stream(stream), queue);
   return hip_status(e, fn);
+}
+
+// A workspace must hold the tile counter: at least mxfp8_grouped_gemm_workspace_bytes().
+static mxfp8_status check_gemm_workspace(const char* fn, void* workspace, size_t bytes) {
+  REQUIRE(workspace != nullptr && bytes >= mxfp8_grouped_gemm_workspace_bytes(),
+          "%s: needs a device workspace of %zu bytes", fn, mxfp8_grouped_gemm_workspace_bytes());
+  return MXFP8_OK;
+}
+
+size_t mxfp8_grouped_gemm_workspace_bytes(void) { return 256; }
+
+mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
+                                const uint8_t* b_data, const uint8_t* b_scale, void* c,
+                                int32_t c_dtype, int64_t T, int64_t N, int64_t K,
+                                const int64_t* m_splits, int32_t G, void* stream) {
+  return grouped_gemm_impl("mxfp8_grouped_gemm", layout, a_data, a_scale, b_data, b_scale, c,
+                           c_dtype, T, N, K, m_splits, G, nullptr, stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm_ws(int32_t layout, const uint8_t* a_data, const uint8_t* a_scale,
+                                   const uint8_t* b_data, const uint8_t* b_scale, void* c,
+                                   int32_t c_dtype, int64_t T, int64_t N, int64_t K,
+                                   const int64_t* m_splits, int32_t G, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* fn = "mxfp8_grouped_gemm_ws";
+  const mxfp8_status s = check_gemm_workspace(fn, workspace, workspace_bytes);
+  if (s != MXFP8_OK) return s;
+  return grouped_gemm_impl(fn, layout, a_data, a_scale, b_data, b_scale, c, c_dtype, T, N, K,
+                           m_splits, G, static_cast<int32_t*>(workspace), stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate(const uint8_t* a_data, const uint8_t* a_scale,
+                                                 const uint8_t* b_data, const uint8_t* b_scale,
+                                                 float* main_grad, int64_t T, int64_t N, int64_t K,
+                                                 const int64_t* m_splits, int32_t G,
+                                                 void* stream) {
+  return wgrad_accumulate_impl("mxfp8_grouped_gemm_wgrad_accumulate", a_data, a_scale, b_data,
+                               b_scale, main_grad, T, N, K, m_splits, G, nullptr, stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm_wgrad_accumulate_ws(const uint8_t* a_data,
+                                                    const uint8_t* a_scale, const uint8_t* b_data,
+                                                    const uint8_t* b_scale, float* main_grad,
+                                                    int64_t T, int64_t N, int64_t K,
+                                                    const int64_t* m_splits, int32_t G,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    void* stream) {
+  const char* fn = "mxfp8_grouped_gemm_wgrad_accumulate_ws";
+  const mxfp8_status s = check_gemm_workspace(fn, workspace, workspace_bytes);
+  if (s != MXFP8_OK) return s;
+  return wgrad_accumulate_impl(fn, a_data, a_scale, b_data, b_scale, main_grad, T, N, K, m_splits,
+                               G, static_cast<int32_t*>(workspace), stream);
 }
 
 mxfp8_status mxfp8_validate_splits(const int64_t* m_splits, int32_t G, int64_t T, int32_t* flag,

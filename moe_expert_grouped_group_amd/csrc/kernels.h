@@ -40,6 +40,6 @@ hipError_t launch_convert_sweep(int32_t mode, uint8_t* out, hipStream_t st);
 hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                const uint8_t* sb, void* c, bool out_bf16, int64_t T, int64_t N,
                                int64_t K, const int64_t* m_splits, int32_t G, bool accumulate,
-                               hipStream_t st);
+                               hipStream_t st, int32_t* queue = nullptr);
 
 }  // namespace mx

@@ -124,6 +124,24 @@ def test_wgrad_accumulate_rejects(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 2000, None) == 1   # G > 1024
 
 
+def test_gemm_workspace_entries_reject(lib):
+    """The workspace forms check the workspace first, then everything the
+    plain forms check."""
+    need = lib.mxfp8_grouped_gemm_workspace_bytes()
+    assert need >= 4
+    g = lib.mxfp8_grouped_gemm_ws
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    st, msg = _status_msg(lib, g(2, *args, 0, 128, 512, 512, FAKE, 1, None, need, None))
+    assert st == 1 and "workspace" in msg                                    # no workspace
+    assert g(2, *args, 0, 128, 512, 512, FAKE, 1, FAKE, need - 1, None) == 1  # too small
+    assert g(3, *args, 0, 128, 512, 512, FAKE, 1, FAKE, need, None) == 1     # bad layout
+    assert g(2, *args, 0, 129, 512, 512, FAKE, 1, FAKE, need, None) == 1     # T % 128
+    f = lib.mxfp8_grouped_gemm_wgrad_accumulate_ws
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 1, None, need, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 128, 512, 512, FAKE, 1, FAKE, need, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 2000, FAKE, need, None) == 1
+
+
 def test_scaled_bias_grad_rejects(lib):
     f = lib.mxfp8_grouped_scaled_bias_grad
     big = 1 << 30

@@ -146,6 +146,42 @@ def test_split_contraction_halves(kind, layout):
             _check(f64(out), ref, mag, torch.float32, win)
 
 
+@pytest.mark.parametrize("case", range(len(CASES) + 1))
+def test_wgrad_tile_counter_same_bytes(case):
+    """The wgrad with a tile counter (mxfp8_grouped_gemm_ws: tiles handed out
+    as workgroups finish) gives the same bytes as the fixed assignment, in
+    fp32 and bf16 and accumulated into main_grad, twice with one workspace.
+    The extra case routes most tokens to one expert of 24 (a few long tiles
+    beside many short ones) with one empty expert: fewer than 1 in 8 experts
+    empty, so its tiles go through the counter; the other cases (1 in 4 or
+    more empty, or a single expert) cover the kernel's choice of the fixed
+    order despite a workspace."""
+    if case < len(CASES):
+        splits, n, k = CASES[case]
+    else:
+        splits, n, k = [0, 3072, 128, 256, 128] + [128] * 19, 1024, 512
+    g, t = len(splits), sum(splits)
+    rng = np.random.default_rng(500 + case)
+    aq, as_ = random_mx(rng, n, t)
+    bq, bs = random_mx(rng, k, t)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    ws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    A, As, B, Bs = dev(aq), dev(as_), dev(bq), dev(bs)
+    log(f"gemm TN tile counter case {case}")
+    for dt in (torch.float32, torch.bfloat16):
+        ref = mx.grouped_gemm("TN", A, As, B, Bs, ms, t, n, k, dt)
+        for _ in range(2):
+            got = mx.grouped_gemm("TN", A, As, B, Bs, ms, t, n, k, dt, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
+    base = torch.from_numpy(rng.standard_normal((g, n, k)).astype(np.float32)).cuda()
+    m1, m2 = base.clone(), base.clone()
+    mx.grouped_gemm_wgrad_accumulate(A, As, B, Bs, ms, t, n, k, m1)
+    mx.grouped_gemm_wgrad_accumulate(A, As, B, Bs, ms, t, n, k, m2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(m1.view(torch.uint8), m2.view(torch.uint8))
+
+
 @pytest.mark.parametrize("kind", ["random", "integer"])
 @pytest.mark.parametrize("case", [0, 2, 4])
 def test_wgrad_accumulate(kind, case):

@@ -25,9 +25,11 @@ pytestmark = pytest.mark.gpu
 class _Step:
     """Input and output buffers of one step, and the step itself."""
 
-    def __init__(self, w, x, wt, dy):
+    def __init__(self, w, x, wt, dy, tile_counter=False):
         g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
         u8 = dict(dtype=torch.uint8, device="cuda")
+        # wgrad tiles handed out through a counter in this workspace, or fixed
+        self.gws = torch.empty(mx.gemm_workspace_bytes(), **u8) if tile_counter else None
         self.shape = (g, t, k, n)
         self.ms = torch.from_numpy(w.m_splits).to("cuda")
         self.x, self.wt, self.dy = x.to("cuda"), wt.to("cuda"), dy.to("cuda")
@@ -60,7 +62,8 @@ class _Step:
         mx.requant_colwise(self.dyo.row_data, self.dyo.row_scale, ms, with_dbias=True,
                            out=self.dyc, dbias=self.db, workspace=self.ws)
         mx.grouped_gemm("TN", self.dyc.col_data, self.dyc.col_scale, self.xc.col_data,
-                        self.xc.col_scale, ms, t, n, k, torch.float32, self.dw)
+                        self.xc.col_scale, ms, t, n, k, torch.float32, self.dw,
+                        workspace=self.gws)
 
     def outputs(self):
         return {"x_row": self.xo.row_data, "x_row_scale": self.xo.row_scale,
@@ -79,9 +82,17 @@ def _inputs(w, i):
     return x, wt, dy
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("tile_counter", [False, True])
+def test_graph_replay_matches_eager(tile_counter):
+    """Replays against eager runs of the fixed-order step; with tile_counter
+    the captured wgrad takes its tiles through a counter in a workspace (reset
+    by a kernel node of the graph on every replay) and must still give the
+    same bytes."""
     w = wl.make("small_moe8")
-    cap = _Step(w, *_inputs(w, 0))
+    if tile_counter:
+        # no empty expert, so the wgrad takes the counter's dynamic order
+        w.m_splits = np.full(w.groups, w.tokens // w.groups, dtype=np.int64)
+    cap = _Step(w, *_inputs(w, 0), tile_counter=tile_counter)
     log("graph: warm-up on a side stream")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -388,6 +388,7 @@ struct UnitPlan {
   int32_t nunits;
   int32_t first_split;   // units from here on are contraction halves
   int32_t dynamic;       // K-grouped: tiles handed out through p.queue
+  int32_t nq;            // counters: 8 (one per XCD) when the grid is a multiple of 8, else 1
 };
 
 // The dynamic wgrad order places long tiles well, but hands out the tiles of
@@ -399,9 +400,10 @@ struct UnitPlan {
 template <bool KGROUPED>
 __device__ __forceinline__ UnitPlan plan_units(const GemmArgs& p, const ExpertTable* t,
                                                int ntiles, int grid) {
-  UnitPlan u{ntiles, ntiles, 0};
+  UnitPlan u{ntiles, ntiles, 0, 1};
   if (KGROUPED) {
     u.dynamic = p.queue != nullptr && 8 * t->nempty < p.G;
+    u.nq = grid % 8 == 0 ? 8 : 1;
     return u;
   }
   if (p.split_tail) {
@@ -616,10 +618,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // every workgroup stops after finitely many tiles.  A global (not
     // generic) atomic: a generic one would also count on the LDS counter the
     // loop waits on.
+    // With a grid that is a multiple of 8 there is one counter per XCD
+    // (workgroup b runs on XCD b % 8): XCD x takes list positions x, x + 8,
+    // ..., so the workgroups sharing its L2 work on neighbouring tiles of the
+    // same experts (one global counter scattered them over the XCDs and
+    // raised the fetched bytes by half).
     int fetched = 0;
     if (KGROUPED && up.dynamic && tid == 0)
-      fetched = __hip_atomic_fetch_add((__attribute__((address_space(1))) int32_t*)p.queue, 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      fetched = __hip_atomic_fetch_add(
+          (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
+          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -764,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       if (tid == 0) next_lds = fetched;
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
-      next = __builtin_amdgcn_readfirstlane(next_lds);
+      next = __builtin_amdgcn_readfirstlane(next_lds) * up.nq + (int)(blockIdx.x & (up.nq - 1));
     }
     TileDesc nxt;
     nxt.nk = 0;
@@ -944,10 +952,16 @@ __global__ __launch_bounds__(kThreads) void zero_split_tail_kernel(GemmArgs p, i
   }
 }
 
-// Sets the wgrad's tile counter to the grid size (the first tiles are the
-// workgroups' own indices), before the GEMM on the same stream.
+// Sets the wgrad's tile counters before the GEMM on the same stream: the
+// first tiles are the workgroups' own indices, so with one counter per XCD
+// (grid a multiple of 8) each starts at grid / 8, else the one counter at
+// the grid size.
 __global__ void queue_init_kernel(int32_t* queue, int32_t grid) {
-  if (threadIdx.x == 0) *queue = grid;
+  if (grid % 8 == 0) {
+    if (threadIdx.x < 8) queue[threadIdx.x] = grid / 8;
+  } else if (threadIdx.x == 0) {
+    queue[0] = grid;
+  }
 }
 
 template <bool KG, bool BF, bool ACC = false>

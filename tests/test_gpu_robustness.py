@@ -1,0 +1,160 @@
+"""Robustness of the hot path through the C ABI: no write outside an output
+(guard bands around every output buffer), the same bytes on a second run
+(determinism), and the pages' check for weights that differ by powers of
+two: results bit-exact up to those scales ([P3545] last commit message: the
+fake distributed weights carry distinct powers of two and the results must
+match exactly up to them).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_group_amd as mx
+from moe_expert_grouped_group_amd import workloads as wl
+
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 256          # bytes of canary before and after every output
+CANARY = 0xA5
+
+
+class _Guarded:
+    """Output buffers carved out of larger device buffers whose margins hold
+    a canary byte."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def __call__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        buf = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+        self.bufs.append(buf)
+        return buf[GUARD:GUARD + n].view(dtype).view(shape)
+
+    def check(self):
+        for i, b in enumerate(self.bufs):
+            assert torch.all(b[:GUARD] == CANARY) and torch.all(b[-GUARD:] == CANARY), i
+
+
+def _mx(g, rows, cols, row=True, col=True):
+    u8 = torch.uint8
+    return mx.MXFP8Tensor(g((rows, cols), u8) if row else None,
+                          g((rows, cols // 32), u8) if row else None,
+                          g((cols, rows), u8) if col else None,
+                          g((cols, rows // 32), u8) if col else None)
+
+
+def _run_all(w, x, wt, dy, h, g):
+    """Every entry point once on guarded outputs; returns the outputs."""
+    G, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    ms = torch.from_numpy(w.m_splits).cuda()
+    f32, bf = torch.float32, torch.bfloat16
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    out = {}
+    xo = mx.group_quantize(x, mx.ROWWISE, out=_mx(g, t, k, col=False))
+    wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=_mx(g, G * n, k))
+    dyo = mx.group_quantize(dy, mx.ROWWISE, out=_mx(g, t, n, col=False))
+    xc = mx.requant_colwise(xo.row_data, xo.row_scale, out=_mx(g, t, k, row=False))
+    dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True,
+                                 out=_mx(g, t, n, row=False), dbias=g((G, n), f32))
+    db2 = mx.grouped_dbias(dyo.row_data, dyo.row_scale, ms, dbias=g((G, n), f32))
+    sc = torch.linspace(0.5, 1.5, t, device="cuda")
+    bias = torch.linspace(-1.0, 1.0, G * n, device="cuda").view(G, n)
+    sdb, sds = mx.grouped_scaled_bias_grad(dyo.row_data, dyo.row_scale, ms, sc, bias,
+                                           out=(g((G, n), f32), g((t,), f32)))
+    y = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
+                        f32, g((t, n), f32))
+    dx = mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n,
+                         k, bf, g((t, k), bf))
+    dw = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k,
+                         f32, g((G, n, k), f32))
+    ws = torch.empty(mx.gemm_workspace_bytes(), **u8)
+    dw2 = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n,
+                          k, bf, g((G, n, k), bf), workspace=ws)
+    mg = g((G, n, k), f32)
+    mg.fill_(0.25)
+    mx.grouped_gemm_wgrad_accumulate(dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms,
+                                     t, n, k, mg, workspace=ws)
+    f = h.shape[1] // 2
+    a = mx.swiglu_fwd(h, out=g((t, f), bf))
+    dh = mx.swiglu_bwd(h, a, out=g((t, 2 * f), bf))
+    ao = mx.swiglu_quantize(h, out=_mx(g, t, f))
+    torch.cuda.synchronize()
+    for name, v in (("xo", xo), ("wo", wo), ("dyo", dyo), ("xc", xc), ("dyc", dyc), ("ao", ao)):
+        for part in ("row_data", "row_scale", "col_data", "col_scale"):
+            if getattr(v, part) is not None:
+                out[f"{name}.{part}"] = getattr(v, part).clone()
+    for name, v in (("db", db), ("db2", db2), ("sdb", sdb), ("sds", sds), ("y", y), ("dx", dx),
+                    ("dw", dw), ("dw2", dw2), ("mg", mg), ("a", a), ("dh", dh)):
+        out[name] = v.clone()
+    return out
+
+
+@pytest.mark.parametrize("name", ["small_moe8", "small_skewed"])
+def test_guard_bands_and_run_twice(name):
+    """No entry point writes outside its outputs (a canary margin on both
+    sides of every output stays intact, also around experts without tokens),
+    and a second run gives the same bytes (every reduction runs in a fixed
+    order; the wgrad's tile counter only changes which workgroup computes a
+    tile)."""
+    w = wl.make(name)
+    x, wt, dy = (w.tensors[nm].cuda() for nm in ("x", "w", "dy"))
+    h = wl.bf16_normal([w.wid, wl.STREAM_DY, 77], (w.tokens, 1024)).cuda()
+    runs = []
+    for i in range(2):
+        g = _Guarded()
+        log(f"robustness {name}: run {i}")
+        runs.append(_run_all(w, x, wt, dy, h, g))
+        g.check()
+    for key in runs[0]:
+        a, b = runs[0][key], runs[1][key]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), key
+
+
+@pytest.mark.parametrize("j", [-3, 5])
+def test_power_of_two_weights_bit_exact_up_to_scale(j):
+    """Weights 2^j W quantize to the same codes with every scale byte j
+    higher, and forward and dgrad give exactly 2^j times the outputs for W;
+    X scaled by 2^j scales the forward output and the weight gradient by
+    exactly 2^j (fp32 outputs; no value reaches the fp32 range limits)."""
+    w = wl.make("small_moe8")
+    G, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
+    ms = torch.from_numpy(w.m_splits).cuda()
+    x, wt, dy = (w.tensors[nm].cuda() for nm in ("x", "w", "dy"))
+    s = 2.0 ** j
+    log(f"power-of-two weights 2^{j}")
+    wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE)
+    wo2 = mx.group_quantize((wt.float() * s).to(torch.bfloat16), mx.ROWWISE | mx.COLWISE)
+    xo = mx.group_quantize(x, mx.ROWWISE)
+    xo2 = mx.group_quantize((x.float() * s).to(torch.bfloat16), mx.ROWWISE)
+    dyo = mx.group_quantize(dy, mx.ROWWISE)
+    torch.cuda.synchronize()
+    assert torch.equal(wo2.row_data, wo.row_data) and torch.equal(wo2.col_data, wo.col_data)
+    assert torch.equal(wo2.row_scale.int(), wo.row_scale.int() + j)
+    assert torch.equal(wo2.col_scale.int(), wo.col_scale.int() + j)
+    f32 = torch.float32
+
+    def fwd(xq, wq):
+        return mx.grouped_gemm("NT", xq.row_data, xq.row_scale, wq.row_data, wq.row_scale, ms, t,
+                               n, k, f32)
+
+    def dgrad(wq):
+        return mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wq.col_data, wq.col_scale, ms,
+                               t, n, k, f32)
+
+    def wgrad(xq):
+        xc = mx.requant_colwise(xq.row_data, xq.row_scale)
+        dyc = mx.requant_colwise(dyo.row_data, dyo.row_scale)
+        return mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms,
+                               t, n, k, f32)
+
+    y, y_w, y_x = fwd(xo, wo), fwd(xo, wo2), fwd(xo2, wo)
+    dx, dx_w = dgrad(wo), dgrad(wo2)
+    dw, dw_x = wgrad(xo), wgrad(xo2)
+    torch.cuda.synchronize()
+    assert torch.equal(y_w, y * s) and torch.equal(y_x, y * s)
+    assert torch.equal(dx_w, dx * s)
+    assert torch.equal(dw_x, dw * s)

@@ -25,6 +25,7 @@ import moe_expert_grouped_group_amd as mx
 from moe_expert_grouped_group_amd import workloads as wl
 from oracle import gemm as og
 from oracle import mxfp8 as om
+from oracle import swiglu as osw
 
 from gpu_util import dev, f64, log, u8
 
@@ -199,3 +200,117 @@ def test_fullsize_group_quantize():
         zr = torch.from_numpy(zero_rows[:64]).cuda()
         assert torch.all(xo.row_scale[zr, 0] == 0)
         assert torch.all((xo.row_data[zr, :32] & 0x7F) == 0)
+
+
+def _near_codes(gpu, ref):
+    g = gpu.astype(np.int32)
+    r = ref.astype(np.int32)
+    return (((g ^ r) & 0x80) == 0) & (np.abs((g & 0x7F) - (r & 0x7F)) <= 1)
+
+
+def _swiglu_bytes_close(q_gpu, s_gpu, q_ref, s_ref):
+    """Quantized SwiGLU bytes: equal except where the device's fp32 SiLU put
+    an activation one bf16 step from the oracle's (a code one step off, or a
+    block scale one off at a power of two), rarely."""
+    ds = s_gpu.astype(np.int32) - s_ref.astype(np.int32)
+    assert np.abs(ds).max() <= 1
+    assert np.count_nonzero(ds) <= max(2, s_ref.size // 1000)
+    diff = (q_gpu != q_ref) & np.repeat(ds == 0, 32, axis=1)
+    assert _near_codes(q_gpu[diff], q_ref[diff]).all()
+    assert np.count_nonzero(diff) <= max(4, q_ref.size // 1000)
+
+
+def test_fullsize_fused_mlp_fc2_and_swiglu():
+    """cfg3 past FC1, at full size in the launch configuration bench.py times:
+    the SwiGLU + quantize of the FC1 output, FC2 forward, FC2 dgrad and wgrad
+    (the wgrad with the tile counter) and the SwiGLU backward.  Stage-wise:
+    each oracle step takes the GPU's output of the step before (h, the
+    quantized activation, da), on sampled rows, 32-token blocks and entries."""
+    name = "nemotron_proxy_mlp"
+    w = wl.make(name)
+    g, t, k, n2 = w.groups, w.tokens, w.hidden, w.ffn
+    f = n2 // 2
+    splits = [int(v) for v in w.m_splits]
+    offs = _offsets(splits)
+    rng = np.random.default_rng(25)
+    ms = dev(w.m_splits)
+    bf = torch.bfloat16
+    log(f"full-size {name}: FC1, SwiGLU + quantize, FC2")
+    xo = mx.group_quantize(w.tensors["x"].to("cuda"), mx.ROWWISE)
+    w1o = mx.group_quantize(w.tensors["w"].to("cuda"), mx.ROWWISE)
+    w2o = mx.group_quantize(w.tensors["w2"].to("cuda"), mx.ROWWISE | mx.COLWISE)
+    h = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale, ms, t, n2,
+                        k, bf)
+    del xo, w1o
+    ao = mx.swiglu_quantize(h)
+    y = mx.grouped_gemm("NT", ao.row_data, ao.row_scale, w2o.row_data, w2o.row_scale, ms, t, k, f,
+                        bf)
+    log(f"full-size {name}: FC2 backward, SwiGLU backward")
+    dyo = mx.group_quantize(w.tensors["dy"].to("cuda"), mx.ROWWISE)
+    dyc = mx.requant_colwise(dyo.row_data, dyo.row_scale)
+    da = mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, w2o.col_data, w2o.col_scale, ms, t, k,
+                         f, bf)
+    ws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    dw2 = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, ao.col_data, ao.col_scale, ms, t, k,
+                          f, bf, workspace=ws)
+    dh = mx.swiglu_bwd(h, da)
+    torch.cuda.synchronize()
+    w2_t, dy_t = w.tensors["w2"], w.tensors["dy"]
+
+    # SwiGLU + quantize: 256 sampled rows (row-wise), two 128-token blocks (column-wise)
+    rows = torch.from_numpy(np.sort(rng.choice(t, size=256, replace=False))).cuda()
+    a_ref = om.round_to_bf16(osw.swiglu_fwd(f64(h[rows])))
+    qr, sr = om.quantize_rowwise(a_ref)
+    _swiglu_bytes_close(u8(ao.row_data[rows]), u8(ao.row_scale[rows]), qr, sr)
+    for b in np.sort(rng.choice(t // 128, size=2, replace=False)):
+        blk = om.round_to_bf16(osw.swiglu_fwd(f64(h[b * 128:(b + 1) * 128])))
+        cq, cs = om.quantize_colwise(blk, [128])
+        _swiglu_bytes_close(u8(ao.col_data[:, b * 128:(b + 1) * 128]),
+                            u8(ao.col_scale[:, 4 * b:4 * b + 4]), cq, cs)
+
+    for e in _window_experts(splits, rng):
+        win = slice(int(offs[e]), int(offs[e]) + 128)
+        # FC2 forward on the GPU's quantized activation (SwiGLU-fed: window bound)
+        cols = np.sort(rng.choice(k, size=64, replace=False))
+        wq, wsc = om.quantize_rowwise(_bf(w2_t[e][torch.from_numpy(cols)]))
+        assert np.array_equal(u8(w2o.row_data[e * k + torch.from_numpy(cols).cuda()]), wq)
+        ref, mag, wn = og.fprop(u8(ao.row_data[win]), u8(ao.row_scale[win]), wq[None], wsc[None],
+                                [128], True, True)
+        log(f"full-size {name}: FC2 forward rows of expert {e}")
+        _check(f64(y[win][:, torch.from_numpy(cols).cuda()]), ref, mag, bf, wn)
+        # FC2 dgrad: dOut rows (oracle quantize) times the column-wise W2 copy
+        dyq, dys = om.quantize_rowwise(_bf(dy_t[win]))
+        assert np.array_equal(u8(dyo.row_data[win]), dyq)
+        fcols = np.sort(rng.choice(f, size=64, replace=False))
+        wcol = _bf(w2_t[:, :, torch.from_numpy(fcols)].reshape(g * k, fcols.size))
+        wcq, wcs = om.quantize_colwise(wcol, [g * k])
+        assert np.array_equal(u8(w2o.col_data[torch.from_numpy(fcols).cuda()]), wcq)
+        one = [128 if gi == e else 0 for gi in range(g)]
+        ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, one, g, True)
+        log(f"full-size {name}: FC2 dgrad rows of expert {e}")
+        _check(f64(da[win][:, torch.from_numpy(fcols).cuda()]), ref2, mag2, bf)
+        # SwiGLU backward on the GPU's h and da rows
+        assert og.within_bf16_ulp(f64(dh[win]), osw.swiglu_bwd(f64(h[win]), f64(da[win]))).all()
+
+    # FC2 wgrad: 64 x 64 entries of every expert, from the dOut column blocks
+    # (oracle requant) and the GPU's column-wise activation blocks
+    kb = np.sort(rng.choice(k // 32, size=2, replace=False))
+    fb = np.sort(rng.choice(f // 32, size=2, replace=False))
+    dycq, dycs = [], []
+    for b in kb:
+        q, s = om.quantize_rowwise(_bf(dy_t[:, b * 32:(b + 1) * 32]))
+        cq, cs = om.requant_colwise(q, s, splits)
+        assert np.array_equal(u8(dyc.col_data[b * 32:(b + 1) * 32]), cq)
+        dycq.append(cq)
+        dycs.append(cs)
+    acq = [u8(ao.col_data[b * 32:(b + 1) * 32]) for b in fb]
+    acs = [u8(ao.col_scale[b * 32:(b + 1) * 32]) for b in fb]
+    ref3, mag3, win3 = og.wgrad(np.concatenate(dycq), np.concatenate(dycs), np.concatenate(acq),
+                                np.concatenate(acs), splits, True, True)
+    ksel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in kb])).cuda()
+    fsel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in fb])).cuda()
+    log(f"full-size {name}: FC2 wgrad samples")
+    _check(f64(dw2[:, ksel][:, :, fsel]), ref3, mag3, bf, win3)
+    for gi, m in enumerate(splits):
+        if m == 0:
+            assert torch.count_nonzero(dw2[gi]).item() == 0, f"expert {gi} has no tokens"

@@ -613,9 +613,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // Dynamic order (wgrad with a tile counter): thread 0 takes the index of
     // this workgroup's next tile now; the value is first needed after the K
     // loop, where every copy has landed, so waiting for it costs nothing.
-    // The counter starts at the grid size (the first tiles are the
-    // workgroups' own indices); an index past the last tile ends the loop, so
-    // every workgroup stops after finitely many tiles.  A global (not
+    // The counters start past the workgroups' first tiles (their own
+    // indices, queue_init_kernel); an index past the last tile ends the loop,
+    // so every workgroup stops after finitely many tiles.  A global (not
     // generic) atomic: a generic one would also count on the LDS counter the
     // loop waits on.
     // With a grid that is a multiple of 8 there is one counter per XCD

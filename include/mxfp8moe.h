@@ -149,6 +149,27 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mxfp8_group_quantize_requant -- mxfp8_group_quantize(ROWWISE) followed by
+ * mxfp8_requant_colwise (with its optional dbias) in one pass over x: the
+ * backward's gradient is quantized row-wise for dgrad, and its column-wise
+ * copy for wgrad is requantized from those row-wise values, not quantized
+ * from bf16 ([P3244] Description and Greptile flowchart: dequantize, then
+ * column-wise requantize, with the bias reductions from the dequantized
+ * grad).  x is read once instead of the row-wise codes being read back.
+ *  x: bf16 [T, K]; q_row/s_row: [T, K] + [T, K/32]; q_col/s_col: the
+ *  transposed column-wise copy [K, T] + [K, T/32]; dbias, m_splits, G,
+ *  workspace as for mxfp8_requant_colwise.
+ *  Every output byte (and dbias, bit for bit) equals what the two calls give.
+ * Errors: EINVAL for NULL pointers (T > 0), T % 128, K % 512, and as
+ * mxfp8_requant_colwise for dbias.
+ */
+mxfp8_status mxfp8_group_quantize_requant(const uint16_t* x, int64_t T, int64_t K,
+                                          uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                          uint8_t* s_col, const int64_t* m_splits, int32_t G,
+                                          float* dbias, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
  * mxfp8_grouped_dbias -- grouped bias gradient from row-wise MXFP8 dY with no
  * column-wise copy (the frozen-weight case: [P3244] Greptile Summary, dbias
  * reduced without a wgrad stage).

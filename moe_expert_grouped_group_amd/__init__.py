@@ -8,6 +8,6 @@ input generators.
 
 from .binding import (  # noqa: F401
     COLWISE, LAYOUT_NN, LAYOUT_NT, LAYOUT_TN, ROWWISE, MXFP8Tensor, convert_sweep,
-    dbias_workspace_bytes, group_quantize, grouped_dbias, grouped_gemm, grouped_scaled_bias_grad,
+    dbias_workspace_bytes, group_quantize, group_quantize_requant, grouped_dbias, grouped_gemm, grouped_scaled_bias_grad,
     grouped_gemm_wgrad_accumulate, gemm_workspace_bytes, requant_colwise, swiglu_bwd, swiglu_fwd, swiglu_quantize, validate_splits)
 from ._native import load as load_library, lib_path  # noqa: F401

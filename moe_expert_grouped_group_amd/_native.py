@@ -30,6 +30,8 @@ SIGNATURES = {
                                       c_vp, c_size, c_vp]),
     "mxfp8_grouped_dbias": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_size,
                                     c_vp]),
+    "mxfp8_group_quantize_requant": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_i32, c_vp, c_vp, c_size, c_vp]),
     "mxfp8_grouped_gemm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64,
                                    c_i64, c_vp, c_i32, c_vp]),
     "mxfp8_validate_splits": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp]),
@@ -50,7 +52,7 @@ SIGNATURES = {
     "mxfp8_convert_sweep": (c_i32, [c_i32, c_vp, c_size, c_vp]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 MXFP8_OK, MXFP8_EINVAL, MXFP8_ENOTSUP, MXFP8_EHIP = 0, 1, 2, 3
 

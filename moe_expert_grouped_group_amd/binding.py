@@ -188,6 +188,34 @@ def requant_colwise(row_data, row_scale, m_splits=None, with_dbias=False, out=No
     return (out, dbias) if with_dbias else out
 
 
+def group_quantize_requant(x, m_splits=None, with_dbias=False, out=None, dbias=None,
+                           workspace=None, stream=None):
+    """bf16 [T, K] -> MXFP8Tensor with the row-wise copy and the column-wise
+    copy requantized from it (+ dbias [G, K] from the dequantized row-wise
+    values), in one pass: the bytes of group_quantize(ROWWISE) followed by
+    requant_colwise.  Returns the tensor, or (tensor, dbias) with_dbias."""
+    lib = _lib()
+    t, k = x.shape
+    _need(x, torch.bfloat16, (t, k), "x")
+    out = _mx_outputs(out, ROWWISE | COLWISE, t, k, x)
+    g = 0
+    ms = None
+    if with_dbias:
+        ms = _splits(m_splits)
+        g = ms.numel()
+        if dbias is None:
+            dbias = _empty((g, k), torch.float32, x)
+        _need(dbias, torch.float32, (g, k), "dbias")
+        workspace = _workspace(t, k, x, workspace)
+    st = lib.mxfp8_group_quantize_requant(
+        _ptr(x), t, k, _ptr(out.row_data), _ptr(out.row_scale), _ptr(out.col_data),
+        _ptr(out.col_scale), _ptr(ms), g, _ptr(dbias) if with_dbias else None,
+        _ptr(workspace) if with_dbias else None,
+        workspace.numel() * workspace.element_size() if with_dbias else 0, _stream(stream))
+    _native.check(st, "mxfp8_group_quantize_requant")
+    return (out, dbias) if with_dbias else out
+
+
 def grouped_dbias(row_data, row_scale, m_splits, dbias=None, workspace=None, stream=None):
     """Row-wise MXFP8 dY [T, N] -> dbias [G, N] fp32 (sum over each expert's rows)."""
     lib = _lib()

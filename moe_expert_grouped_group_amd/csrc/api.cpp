@@ -67,7 +67,7 @@ extern "C" {
 
 const char* mxfp8_last_error(void) { return g_err; }
 
-int32_t mxfp8_abi_version(void) { return 3; }
+int32_t mxfp8_abi_version(void) { return 4; }
 
 size_t mxfp8_dbias_workspace_bytes(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0) return 0;
@@ -118,6 +118,33 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
   hipStream_t st = as_stream(stream);
   hipError_t e = hipSuccess;
   if (T > 0) e = mx::launch_requant_colwise(q_row, s_row, T, K, q_col, s_col, partial, st);
+  if (e == hipSuccess && dbias != nullptr)
+    e = mx::launch_dbias_finalize(partial, m_splits, G, T, K, dbias, st);
+  return hip_status(e, fn);
+}
+
+mxfp8_status mxfp8_group_quantize_requant(const uint16_t* x, int64_t T, int64_t K,
+                                          uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                          uint8_t* s_col, const int64_t* m_splits, int32_t G,
+                                          float* dbias, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  const char* fn = "mxfp8_group_quantize_requant";
+  REQUIRE(T == 0 || (x && q_row && s_row && q_col && s_col), "%s: NULL data/scale pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  float* partial = nullptr;
+  if (dbias != nullptr) {
+    mxfp8_status st = check_device_splits(m_splits, G, fn);
+    if (st != MXFP8_OK) return st;
+    REQUIRE((workspace != nullptr || T == 0) &&
+                workspace_bytes >= mxfp8_dbias_workspace_bytes(T, K),
+            "%s: dbias needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, K));
+    partial = static_cast<float*>(workspace);
+  }
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0) e = mx::launch_quant_row_requant(x, T, K, q_row, s_row, q_col, s_col, partial, st);
   if (e == hipSuccess && dbias != nullptr)
     e = mx::launch_dbias_finalize(partial, m_splits, G, T, K, dbias, st);
   return hip_status(e, fn);

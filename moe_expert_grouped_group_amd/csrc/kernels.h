@@ -15,6 +15,9 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t T, int64_t K, uint8_t
 hipError_t launch_quant_rowcol(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                                const int32_t* noop, hipStream_t st);
+hipError_t launch_quant_row_requant(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
+                                   uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, float* partial,
+                                   hipStream_t st);
 hipError_t launch_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
                                   int64_t K, uint8_t* q_col, uint8_t* s_col, float* partial,
                                   hipStream_t st);

@@ -959,6 +959,64 @@ __global__ __launch_bounds__(kColThreads) void swiglu_quant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// row-wise quantize of bf16 fused with the column-wise requantize of its result
+// ---------------------------------------------------------------------------
+
+// One pass over bf16 x that writes what quant_rowwise_kernel followed by
+// requant_colwise_kernel writes: the row-wise codes and scales, and the
+// column-wise copy requantized from the dequantized row-wise values (+ the
+// per-tile dbias partials), reading x once instead of reading the row-wise
+// codes back.  The tile's row-wise codes and scale operands are staged in LDS
+// in the requantize's layout and requant_tile_fast runs on them unchanged, so
+// the bytes and partial sums are those of the two-kernel path.  Row scale
+// bytes from bf16 data are at most 246 = kMaxFastScaleByte (the largest bf16
+// exponent field, 254, minus 8), so the fast requantize always applies.
+// Persistent like quant_rowcol_kernel: the next tile's loads are issued once
+// this tile is staged.
+template <bool kDbias>
+__global__ __launch_bounds__(kColThreads) void quant_row_requant_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t K, uint8_t* __restrict__ q_row,
+    uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+    float* __restrict__ partial, int32_t ntk, int32_t ntiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytesU8];
+  __shared__ float lds_sc[kLdsScWords];             // row scales as conversion operands
+  const int tid = threadIdx.x;
+  int tile = blockIdx.x;
+  u32x4 w[8];
+  load_bf16_tile(x, K, tile, ntk, w);
+  for (;;) {
+    int64_t k0, t0;
+    tile_origin(tile, ntk, k0, t0);
+    // chunk jj of this thread: row 16 jj + tid / 16, its 8 elements
+    // 8 (tid % 16) .. + 7; the quad of lanes 4b..4b+3 holds block b
+    const uint32_t ro = opaque_u32((uint32_t)(tid >> 4) * (uint32_t)K + (tid & 15) * 8);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int idx = tid + kColThreads * jj;
+      const int r = idx >> 4, cc = idx & 15;
+      const uint4 c = make_uint4(w[jj].x, w[jj].y, w[jj].z, w[jj].w);
+      const uint32_t amax = quad_max(chunk_amax_bits(c));
+      const uint32_t byte = scale_byte_from_exp(amax >> 7);
+      const int64_t rb = t0 * K + k0 + 16 * jj * K;   // uniform
+      const uint2 e = encode_chunk(c, byte);
+      *reinterpret_cast<uint2*>(q_row + rb + ro) = e;
+      *reinterpret_cast<uint2*>(&lds[lds_off_u8(r, cc * 8)]) = e;
+      if ((cc & 3) == 0) lds_sc[lds_sc_idx(r, cc >> 2)] = e8m0_operand(byte);
+      const uint32_t bytes4 = gather_blocks4(byte);
+      if ((tid & 15) == 0)
+        *reinterpret_cast<uint32_t*>(s_row + (rb >> 5) + (ro >> 5)) = bytes4;
+    }
+    __syncthreads();
+    const int next = tile + (int)gridDim.x;
+    if (next < ntiles) load_bf16_tile(x, K, next, ntk, w);
+    requant_tile_fast<kDbias>(lds, lds_sc, T, K, k0, t0, q_col, s_col, partial);
+    if (next >= ntiles) break;
+    __syncthreads();   // every LDS read of this tile is done before the next write
+    tile = next;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -991,6 +1049,7 @@ static int device_cus() {
 // the LDS padding replaced by a swizzle, were 1-5 % slower as well).
 constexpr int kRowcolWgPerCu = 4;
 constexpr int kRequantWgPerCu = 3;
+constexpr int kRowRequantWgPerCu = 4;
 
 hipError_t launch_quant_rowcol(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
@@ -1015,6 +1074,21 @@ hipError_t launch_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, in
   else
     hipLaunchKernelGGL(requant_colwise_kernel<false>, dim3(grid), dim3(kColThreads), 0, st,
                        q_row, s_row, T, K, q_col, s_col, partial, ntk, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row_requant(const uint16_t* x, int64_t T, int64_t K, uint8_t* q_row,
+                                   uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, float* partial,
+                                   hipStream_t st) {
+  const int32_t ntt = (int32_t)(T / kTileT), ntk = (int32_t)(K / kTileK);
+  const int32_t ntiles = ntt * ntk;
+  const int grid = (int)std::min<int64_t>(ntiles, (int64_t)device_cus() * kRowRequantWgPerCu);
+  if (partial != nullptr)
+    hipLaunchKernelGGL(quant_row_requant_kernel<true>, dim3(grid), dim3(kColThreads), 0, st, x, T,
+                       K, q_row, s_row, q_col, s_col, partial, ntk, ntiles);
+  else
+    hipLaunchKernelGGL(quant_row_requant_kernel<false>, dim3(grid), dim3(kColThreads), 0, st, x,
+                       T, K, q_row, s_row, q_col, s_col, partial, ntk, ntiles);
   return hipGetLastError();
 }
 

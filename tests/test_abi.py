@@ -124,6 +124,19 @@ def test_wgrad_accumulate_rejects(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 512, 512, FAKE, 2000, None) == 1   # G > 1024
 
 
+def test_quantize_requant_rejects(lib):
+    f = lib.mxfp8_group_quantize_requant
+    args = (FAKE, FAKE, FAKE, FAKE)
+    assert f(None, 128, 512, *args, None, 0, None, None, 0, None) == 1        # no x
+    assert f(FAKE, 100, 512, *args, None, 0, None, None, 0, None) == 1        # T % 128
+    assert f(FAKE, 128, 500, *args, None, 0, None, None, 0, None) == 1        # K % 512
+    assert f(FAKE, 128, 512, FAKE, None, FAKE, FAKE, None, 0, None, None, 0, None) == 1
+    # dbias without splits, or without a workspace
+    assert f(FAKE, 128, 512, *args, None, 1, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, 128, 512, *args, FAKE, 1, FAKE, None, 0, None) == 1
+    assert f(None, 0, 512, None, None, None, None, None, 0, None, None, 0, None) == 0  # T == 0
+
+
 def test_gemm_workspace_entries_reject(lib):
     """The workspace forms check the workspace first, then everything the
     plain forms check."""

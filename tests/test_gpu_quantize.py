@@ -364,3 +364,53 @@ def test_noop_flag(usage):
         _check_row(x2, out)
     if usage & mx.COLWISE:
         _check_col(x2, out)
+
+
+def _quantize_requant_case(x_cpu, splits, with_dbias):
+    """The fused call against the two calls it replaces (every byte, and dbias
+    bit for bit) and against the oracle's row-wise quantize + requantize."""
+    x = x_cpu.to("cuda")
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    ref = mx.group_quantize(x, mx.ROWWISE)
+    if with_dbias:
+        refc, refdb = mx.requant_colwise(ref.row_data, ref.row_scale, ms, with_dbias=True)
+        got, db = mx.group_quantize_requant(x, ms, with_dbias=True)
+    else:
+        refc = mx.requant_colwise(ref.row_data, ref.row_scale)
+        got = mx.group_quantize_requant(x)
+    torch.cuda.synchronize()
+    for a, b in ((got.row_data, ref.row_data), (got.row_scale, ref.row_scale),
+                 (got.col_data, refc.col_data), (got.col_scale, refc.col_scale)):
+        assert torch.equal(a, b)
+    if with_dbias:
+        assert torch.equal(db.view(torch.uint8), refdb.view(torch.uint8))
+    q, s = om.quantize_rowwise(f64(x_cpu))
+    cq, cs = om.requant_colwise(q, s, splits)
+    assert np.array_equal(u8(got.row_data), q) and np.array_equal(u8(got.row_scale), s)
+    assert np.array_equal(u8(got.col_data), cq) and np.array_equal(u8(got.col_scale), cs)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(256, 512, 31), (640, 1536, 32), (1024, 4096, 33)])
+@pytest.mark.parametrize("with_dbias", [False, True])
+def test_quantize_requant_sweep(rows, cols, seed, with_dbias):
+    """Row-wise quantize fused with the column-wise requantize of its result,
+    on inputs spanning the encoder's relative exponents and whole-range
+    values, with zero blocks; dbias over uneven experts (one empty)."""
+    log(f"quantize+requant sweep {rows}x{cols} dbias {with_dbias}")
+    x = bf16_from_bits(sweep_bf16_bits(rows, cols, seed))
+    splits = [128, 0, rows - 128]
+    _quantize_requant_case(x, splits, with_dbias)
+
+
+def test_quantize_requant_every_bf16_value():
+    log("quantize+requant every bf16 value")
+    x = bf16_from_bits(all_bf16_bits(512))
+    _quantize_requant_case(x, [x.shape[0]], True)
+
+
+@pytest.mark.parametrize("name", ["small_moe8", "small_skewed"])
+def test_quantize_requant_workloads(name):
+    log(f"quantize+requant workload {name}")
+    w = wl.make(name)
+    _quantize_requant_case(w.tensors["dy"], [int(v) for v in w.m_splits], True)
+    _quantize_requant_case(w.tensors["x"], [int(v) for v in w.m_splits], False)

@@ -1,14 +1,14 @@
 """Benchmark of the MXFP8 MoE expert grouped-GEMM hot path on one MI355X.
 
 One step = one pass of the whole hot path of an expert linear over one batch:
-  1. row-wise group quantize of X            [T, K]  bf16 -> MXFP8
+  1. row-wise group quantize of X and the column-wise requantize of the
+     result (saved for wgrad), one fused launch   [T, K]  bf16 -> MXFP8
   2. row + column-wise quantize of W         [G, N, K] bf16 -> MXFP8 (both copies)
   3. forward grouped GEMM (NT)               Y  [T, N] = X W_g^T
-  4. column-wise requantize of X             (saved for wgrad)
-  5. row-wise group quantize of dY           [T, N]
-  6. dgrad grouped GEMM (NN)                 dX [T, K] = dY W_g
-  7. column-wise requantize of dY + dbias    dbias [G, N]
-  8. wgrad grouped GEMM (TN)                 dW [G, N, K] = dY_g^T X_g
+  4. row-wise group quantize of dY, its column-wise requantize and dbias,
+     one fused launch                        [T, N], dbias [G, N]
+  5. dgrad grouped GEMM (NN)                 dX [T, K] = dY W_g
+  6. wgrad grouped GEMM (TN)                 dW [G, N, K] = dY_g^T X_g
 Workload: 8 experts, hidden 4096 -> expert FFN 14336 (one linear), 16384
 tokens routed by a seeded Dirichlet(1) multinomial (multiples of 128); X, dY
 ~ N(0, 1), W ~ N(0, 0.02) in bf16; fp32 GEMM outputs.  Inputs are resident in
@@ -124,7 +124,7 @@ def cpu_baseline(w, budget_rows=4096, n_cols=2048):
 
     Sample: the first `budget_rows` tokens, re-split as 8 experts of 128 rows,
     the first `n_cols` output features of every expert's weight, the full
-    hidden size; the same eight steps as the GPU step.  Returns TFLOP/s of the
+    hidden size; the same steps as the GPU step.  Returns TFLOP/s of the
     three GEMMs over the oracle's whole wall time.
     """
     import numpy as np
@@ -157,7 +157,7 @@ def cpu_baseline(w, budget_rows=4096, n_cols=2048):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{WORKLOAD}: first {rows} tokens as {g} experts x {rows // g}, "
-                      f"{n_cols} of {w.ffn} output features, K={k}; all 8 steps; "
+                      f"{n_cols} of {w.ffn} output features, K={k}; every step of the path; "
                       f"{dt:.2f} s wall, float64 NumPy"}
 
 
@@ -236,8 +236,8 @@ def bench_skewed_linear(steps, warmup):
     xo = mx.group_quantize(x, mx.ROWWISE)
     wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE)
     xc = mx.requant_colwise(xo.row_data, xo.row_scale)
-    dyo = mx.group_quantize(dy, mx.ROWWISE)
-    dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True)
+    dyo, db = mx.group_quantize_requant(dy, ms, with_dbias=True)
+    dyc = dyo
     f32 = torch.float32
     y = torch.empty(t, n, dtype=f32, device="cuda")
     dx = torch.empty(t, k, dtype=f32, device="cuda")
@@ -249,12 +249,10 @@ def bench_skewed_linear(steps, warmup):
         ("gemm_fprop", lambda: mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data,
                                                wo.row_scale, ms, t, n, k, f32, y)),
         ("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)),
-        ("quant_dy", lambda: mx.group_quantize(dy, mx.ROWWISE, out=dyo)),
+        ("quant_requant_dy_dbias", lambda: mx.group_quantize_requant(
+            dy, ms, with_dbias=True, out=dyo, dbias=db, workspace=ws)),
         ("gemm_dgrad", lambda: mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data,
                                                wo.col_scale, ms, t, n, k, f32, dx)),
-        ("requant_dy_dbias", lambda: mx.requant_colwise(dyo.row_data, dyo.row_scale, ms,
-                                                        with_dbias=True, out=dyc, dbias=db,
-                                                        workspace=ws)),
         ("gemm_wgrad", lambda: mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data,
                                                xc.col_scale, ms, t, n, k, f32, dw,
                                                workspace=gws)),
@@ -300,27 +298,27 @@ def bench_fused_mlp(steps, warmup):
     del w
     bf = torch.bfloat16
     R, C = mx.ROWWISE, mx.COLWISE
-    xo = mx.group_quantize(x, R)
+    xo = mx.group_quantize_requant(x)
+    xc = xo
     w1o = mx.group_quantize(w1, R | C)
     w2o = mx.group_quantize(w2, R | C)
     h = torch.empty(t, n2, dtype=bf, device="cuda")
     ao = mx.swiglu_quantize(torch.zeros(t, n2, dtype=bf, device="cuda"), R | C)
     y = torch.empty(t, k, dtype=bf, device="cuda")
-    xc = mx.requant_colwise(xo.row_data, xo.row_scale)
-    dyo = mx.group_quantize(dout, R)
-    dyc = mx.requant_colwise(dyo.row_data, dyo.row_scale)
+    dyo = mx.group_quantize_requant(dout)
+    dyc = dyo
     da = torch.empty(t, f, dtype=bf, device="cuda")
     dw2 = torch.empty(g, k, f, dtype=bf, device="cuda")
     dh = torch.empty(t, n2, dtype=bf, device="cuda")
-    dho = mx.group_quantize(dh.zero_(), R)
-    dhc, db1 = mx.requant_colwise(dho.row_data, dho.row_scale, ms, with_dbias=True)
+    dho, db1 = mx.group_quantize_requant(dh.zero_(), ms, with_dbias=True)
+    dhc = dho
     dx = torch.empty(t, k, dtype=bf, device="cuda")
     dw1 = torch.empty(g, n2, k, dtype=bf, device="cuda")
     ws = torch.empty(mx.dbias_workspace_bytes(t, n2), dtype=torch.uint8, device="cuda")
     gws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
     gemm = mx.grouped_gemm
     launches = [
-        ("quant_x", lambda: mx.group_quantize(x, R, out=xo)),
+        ("quant_requant_x", lambda: mx.group_quantize_requant(x, out=xo)),
         ("quant_w1", lambda: mx.group_quantize(w1, R | C, out=w1o)),
         ("quant_w2", lambda: mx.group_quantize(w2, R | C, out=w2o)),
         ("fc1_fprop", lambda: gemm("NT", xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale,
@@ -328,20 +326,16 @@ def bench_fused_mlp(steps, warmup):
         ("swiglu_quant", lambda: mx.swiglu_quantize(h, R | C, out=ao)),
         ("fc2_fprop", lambda: gemm("NT", ao.row_data, ao.row_scale, w2o.row_data, w2o.row_scale,
                                    ms, t, k, f, bf, y)),
-        ("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)),
-        ("quant_dy", lambda: mx.group_quantize(dout, R, out=dyo)),
+        ("quant_requant_dy", lambda: mx.group_quantize_requant(dout, out=dyo)),
         ("fc2_dgrad", lambda: gemm("NN", dyo.row_data, dyo.row_scale, w2o.col_data,
                                    w2o.col_scale, ms, t, k, f, bf, da)),
-        ("requant_dy", lambda: mx.requant_colwise(dyo.row_data, dyo.row_scale, out=dyc)),
         ("fc2_wgrad", lambda: gemm("TN", dyc.col_data, dyc.col_scale, ao.col_data, ao.col_scale,
                                    ms, t, k, f, bf, dw2, workspace=gws)),
         ("swiglu_bwd", lambda: mx.swiglu_bwd(h, da, out=dh)),
-        ("quant_dh", lambda: mx.group_quantize(dh, R, out=dho)),
+        ("quant_requant_dh_dbias", lambda: mx.group_quantize_requant(
+            dh, ms, with_dbias=True, out=dho, dbias=db1, workspace=ws)),
         ("fc1_dgrad", lambda: gemm("NN", dho.row_data, dho.row_scale, w1o.col_data,
                                    w1o.col_scale, ms, t, n2, k, bf, dx)),
-        ("requant_dh_dbias", lambda: mx.requant_colwise(dho.row_data, dho.row_scale, ms,
-                                                        with_dbias=True, out=dhc, dbias=db1,
-                                                        workspace=ws)),
         ("fc1_wgrad", lambda: gemm("TN", dhc.col_data, dhc.col_scale, xc.col_data, xc.col_scale,
                                    ms, t, n2, k, bf, dw1, workspace=gws)),
     ]
@@ -409,12 +403,16 @@ def main():
     out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
 
     u8 = dict(dtype=torch.uint8, device=dev)
-    xo = mx.MXFP8Tensor(torch.empty(t, k, **u8), torch.empty(t, k // 32, **u8))
+    # row-wise copies (forward, dgrad) and the column-wise requantized copies
+    # (wgrad) of X and dY, written by one fused launch each
+    xo = mx.MXFP8Tensor(torch.empty(t, k, **u8), torch.empty(t, k // 32, **u8),
+                        torch.empty(k, t, **u8), torch.empty(k, t // 32, **u8))
     wo = mx.MXFP8Tensor(torch.empty(g * n, k, **u8), torch.empty(g * n, k // 32, **u8),
                         torch.empty(k, g * n, **u8), torch.empty(k, g * n // 32, **u8))
-    xc = mx.MXFP8Tensor(col_data=torch.empty(k, t, **u8), col_scale=torch.empty(k, t // 32, **u8))
-    dyo = mx.MXFP8Tensor(torch.empty(t, n, **u8), torch.empty(t, n // 32, **u8))
-    dyc = mx.MXFP8Tensor(col_data=torch.empty(n, t, **u8), col_scale=torch.empty(n, t // 32, **u8))
+    xc = xo
+    dyo = mx.MXFP8Tensor(torch.empty(t, n, **u8), torch.empty(t, n // 32, **u8),
+                         torch.empty(n, t, **u8), torch.empty(n, t // 32, **u8))
+    dyc = dyo
     y = torch.empty(t, n, dtype=out_dtype, device=dev)
     dx = torch.empty(t, k, dtype=out_dtype, device=dev)
     dw = torch.empty(g, n, k, dtype=out_dtype, device=dev)
@@ -434,31 +432,26 @@ def main():
         return r
 
     def step_plain():
-        mx.group_quantize(x, mx.ROWWISE, out=xo)
+        mx.group_quantize_requant(x, out=xo)
         mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo)
         mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
                         out_dtype, y)
-        mx.requant_colwise(xo.row_data, xo.row_scale, out=xc)
-        mx.group_quantize(dy, mx.ROWWISE, out=dyo)
+        mx.group_quantize_requant(dy, ms, with_dbias=True, out=dyo, dbias=db, workspace=ws)
         mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n, k,
                         out_dtype, dx)
-        mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db,
-                           workspace=ws)
         mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k,
                         out_dtype, dw, workspace=gws)
 
     def step():
-        timed("quant_x", lambda: mx.group_quantize(x, mx.ROWWISE, out=xo))
+        timed("quant_requant_x", lambda: mx.group_quantize_requant(x, out=xo))
         timed("quant_w", lambda: mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE, out=wo))
         timed("gemm_fprop", lambda: mx.grouped_gemm(
             "NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k, out_dtype, y))
-        timed("requant_x", lambda: mx.requant_colwise(xo.row_data, xo.row_scale, out=xc))
-        timed("quant_dy", lambda: mx.group_quantize(dy, mx.ROWWISE, out=dyo))
+        timed("quant_requant_dy_dbias", lambda: mx.group_quantize_requant(
+            dy, ms, with_dbias=True, out=dyo, dbias=db, workspace=ws))
         timed("gemm_dgrad", lambda: mx.grouped_gemm(
             "NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n, k, out_dtype,
             dx))
-        timed("requant_dy_dbias", lambda: mx.requant_colwise(
-            dyo.row_data, dyo.row_scale, ms, with_dbias=True, out=dyc, dbias=db, workspace=ws))
         timed("gemm_wgrad", lambda: mx.grouped_gemm(
             "TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, out_dtype,
             dw, workspace=gws))
@@ -483,7 +476,7 @@ def main():
     per = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
 
     if not args.eager:
-        # The timed steps again, replayed from a HIP graph of the same eight
+        # The timed steps again, replayed from a HIP graph of the same six
         # launches (captured once; every output buffer is caller-owned, so a
         # replay rewrites the same memory): no host launch gaps between the
         # kernels.  The per-launch times above come from the eager steps.
@@ -555,11 +548,9 @@ def main():
     value = 3 * flop_one / (ms_step * 1e-3) / 1e12
     # algorithmic HBM bytes of the streaming kernels
     q_bytes = {
-        "quant_x": t * k * (2 + 1 + 1 / 32),
+        "quant_requant_x": t * k * (2 + 2 * (1 + 1 / 32)),
         "quant_w": g * n * k * (2 + 2 * (1 + 1 / 32)),
-        "requant_x": t * k * 2 * (1 + 1 / 32),
-        "quant_dy": t * n * (2 + 1 + 1 / 32),
-        "requant_dy_dbias": t * n * 2 * (1 + 1 / 32) + t * n * 4 / 128 * 2 + g * n * 4,
+        "quant_requant_dy_dbias": t * n * (2 + 2 * (1 + 1 / 32)) + t * n * 4 / 128 * 2 + g * n * 4,
     }
     quant_ms = sum(per[nm] for nm in q_bytes)
     quant_gbs = sum(q_bytes.values()) / (quant_ms * 1e-3) / 1e9

@@ -25,11 +25,13 @@ pytestmark = pytest.mark.gpu
 class _Step:
     """Input and output buffers of one step, and the step itself."""
 
-    def __init__(self, w, x, wt, dy, tile_counter=False):
+    def __init__(self, w, x, wt, dy, tile_counter=False, fused=False):
         g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
         u8 = dict(dtype=torch.uint8, device="cuda")
         # wgrad tiles handed out through a counter in this workspace, or fixed
         self.gws = torch.empty(mx.gemm_workspace_bytes(), **u8) if tile_counter else None
+        # X and dY quantized row-wise and requantized column-wise in one launch each
+        self.fused = fused
         self.shape = (g, t, k, n)
         self.ms = torch.from_numpy(w.m_splits).to("cuda")
         self.x, self.wt, self.dy = x.to("cuda"), wt.to("cuda"), dy.to("cuda")
@@ -47,20 +49,31 @@ class _Step:
         self.dw = torch.empty(g, n, k, **f32)
         self.db = torch.empty(g, n, **f32)
         self.ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8)
+        if fused:
+            self.xo.col_data, self.xo.col_scale = self.xc.col_data, self.xc.col_scale
+            self.dyo.col_data, self.dyo.col_scale = self.dyc.col_data, self.dyc.col_scale
 
     def run(self):
         g, t, k, n = self.shape
         ms = self.ms
-        mx.group_quantize(self.x, mx.ROWWISE, out=self.xo)
+        if self.fused:
+            mx.group_quantize_requant(self.x, out=self.xo)
+        else:
+            mx.group_quantize(self.x, mx.ROWWISE, out=self.xo)
         mx.group_quantize(self.wt, mx.ROWWISE | mx.COLWISE, out=self.wo)
         mx.grouped_gemm("NT", self.xo.row_data, self.xo.row_scale, self.wo.row_data,
                         self.wo.row_scale, ms, t, n, k, torch.float32, self.y)
-        mx.requant_colwise(self.xo.row_data, self.xo.row_scale, out=self.xc)
-        mx.group_quantize(self.dy, mx.ROWWISE, out=self.dyo)
+        if self.fused:
+            mx.group_quantize_requant(self.dy, ms, with_dbias=True, out=self.dyo, dbias=self.db,
+                                      workspace=self.ws)
+        else:
+            mx.requant_colwise(self.xo.row_data, self.xo.row_scale, out=self.xc)
+            mx.group_quantize(self.dy, mx.ROWWISE, out=self.dyo)
         mx.grouped_gemm("NN", self.dyo.row_data, self.dyo.row_scale, self.wo.col_data,
                         self.wo.col_scale, ms, t, n, k, torch.float32, self.dx)
-        mx.requant_colwise(self.dyo.row_data, self.dyo.row_scale, ms, with_dbias=True,
-                           out=self.dyc, dbias=self.db, workspace=self.ws)
+        if not self.fused:
+            mx.requant_colwise(self.dyo.row_data, self.dyo.row_scale, ms, with_dbias=True,
+                               out=self.dyc, dbias=self.db, workspace=self.ws)
         mx.grouped_gemm("TN", self.dyc.col_data, self.dyc.col_scale, self.xc.col_data,
                         self.xc.col_scale, ms, t, n, k, torch.float32, self.dw,
                         workspace=self.gws)
@@ -84,15 +97,16 @@ def _inputs(w, i):
 
 @pytest.mark.parametrize("tile_counter", [False, True])
 def test_graph_replay_matches_eager(tile_counter):
-    """Replays against eager runs of the fixed-order step; with tile_counter
-    the captured wgrad takes its tiles through a counter in a workspace (reset
-    by a kernel node of the graph on every replay) and must still give the
-    same bytes."""
+    """Replays against eager runs of the fixed-order, unfused step; with
+    tile_counter the captured step is the one bench.py replays: the wgrad
+    takes its tiles through a counter in a workspace (reset by a kernel node
+    of the graph on every replay) and X and dY go through the fused quantize
+    + requantize; every replay must still give the same bytes."""
     w = wl.make("small_moe8")
     if tile_counter:
         # no empty expert, so the wgrad takes the counter's dynamic order
         w.m_splits = np.full(w.groups, w.tokens // w.groups, dtype=np.int64)
-    cap = _Step(w, *_inputs(w, 0), tile_counter=tile_counter)
+    cap = _Step(w, *_inputs(w, 0), tile_counter=tile_counter, fused=tile_counter)
     log("graph: warm-up on a side stream")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -606,6 +606,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   TileDesc cur = describe_unit<KGROUPED>(p, &table, up, tile, esz);
   setup(cur);
   tile_prologue(cur.nk);
+  // A tile's first wait leaves 63 vector-memory operations outstanding.  It
+  // sees stages 0 and 1 land when at least 63 operations were issued after
+  // them (the previous tile's stores: the counter completes in issue order),
+  // and up to 63 of those stores then drain behind the first MFMA step; a
+  // wait for stage 0 alone drained nearly every store before the first MFMA.
+  // Where fewer operations follow them (the first tile, and after a tile
+  // whose epilogue stores fewer), a full wait right after the copies or the
+  // stores stands in.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   for (;;) {
     const int nk = cur.nk;
@@ -636,13 +645,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     if (nk > 0) {
-      // stage 0: only the copies of stage 1 (if any) were issued after it
-      // (copies complete in issue order; stores of the previous tile can only
-      // make this wait longer)
-      if (ns > 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaHalf));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // stages 0 and 1 landed (the wait before the tile loop explains 63)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(63));
       __syncthreads();
       // step 0 through an opaque index: with constant offsets its addresses
       // would be precomputed once and spilled, and the reload's wait counts
@@ -925,6 +929,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       }
     }
     if (next >= up.nunits) break;
+    // the store loops above issue one operation per register (M-grouped: 256
+    // per wave, every row inside the tile) or per 4 registers (K-grouped: 64
+    // stores, plus 64 loads when accumulating)
+    if (!(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     tile = next;
     cur = nxt;
   }

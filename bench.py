@@ -36,7 +36,9 @@ workspace (mxfp8_grouped_gemm_ws), with which the kernel hands out the wgrad
 tiles dynamically unless 1 expert in 8 or more has no token.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
+       python bench.py --only NAME           (one of the other workloads alone)
        python bench.py --calibrate-copy      (copy of 1 GiB, for counter scaling)
+       python bench.py --summarize trace|traffic ...   (profiles/ tables from rocprofv3 CSVs)
 """
 
 import argparse
@@ -72,6 +74,12 @@ def parse():
                          "standalone group quantize)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (counter scaling)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the headline step (no launches outside it, no other "
+                         "workloads, no CPU baseline): for per-step profiles")
+    ap.add_argument("--only", choices=sorted(OTHERS),
+                    help="time only this one of the other workloads and print its record "
+                         "(for per-workload profiles)")
     return ap.parse_args()
 
 
@@ -122,10 +130,12 @@ def calibrate_copy():
 def cpu_baseline(w, budget_rows=4096, n_cols=2048):
     """Time the CPU oracle on a bounded sample of the same workload.
 
-    Sample: the first `budget_rows` tokens, re-split as 8 experts of 128 rows,
-    the first `n_cols` output features of every expert's weight, the full
-    hidden size; the same steps as the GPU step.  Returns TFLOP/s of the
-    three GEMMs over the oracle's whole wall time.
+    Sample: the first `budget_rows` tokens, re-split as 8 experts of
+    budget_rows / 8 = 512 rows each, the first `n_cols` output features of
+    every expert's weight, the full hidden size; the same steps as the GPU
+    step, each timed on its own.  Returns TFLOP/s of the three GEMMs over the
+    oracle's whole wall time, the per-step seconds, the cores the process may
+    run on (sched_getaffinity), the BLAS library and its thread count.
     """
     import numpy as np
     import threadpoolctl
@@ -140,25 +150,43 @@ def cpu_baseline(w, budget_rows=4096, n_cols=2048):
     x = w.tensors["x"][:rows].double().numpy()
     wt = w.tensors["w"][:, :n_cols, :].double().numpy().reshape(g * n_cols, k)
     dy = w.tensors["dy"][:rows, :n_cols].double().numpy()
-    t0 = time.perf_counter()
-    xq, xs = om.quantize_rowwise(x)
-    wq, ws = om.quantize_rowwise(wt)
-    wcq, wcs = om.quantize_colwise(wt, [g * n_cols])
-    _y = og.fprop(xq, xs, wq.reshape(g, n_cols, k), ws.reshape(g, n_cols, k // 32), splits)
-    xcq, xcs = om.requant_colwise(xq, xs, splits)
-    dyq, dys = om.quantize_rowwise(dy)
-    _dx = og.dgrad(dyq, dys, wcq, wcs, splits, g)
-    dycq, dycs = om.requant_colwise(dyq, dys, splits)
-    _db = om.grouped_dbias(dyq, dys, splits)
-    _dw = og.wgrad(dycq, dycs, xcq, xcs, splits)
-    dt = time.perf_counter() - t0
+    ops = {}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        ops[name] = round(time.perf_counter() - t0, 3)
+        return r
+
+    xq, xs = timed("quantize_x_rowwise", lambda: om.quantize_rowwise(x))
+    wq, ws = timed("quantize_w_rowwise", lambda: om.quantize_rowwise(wt))
+    wcq, wcs = timed("quantize_w_colwise", lambda: om.quantize_colwise(wt, [g * n_cols]))
+    timed("fprop", lambda: og.fprop(xq, xs, wq.reshape(g, n_cols, k),
+                                    ws.reshape(g, n_cols, k // 32), splits))
+    xcq, xcs = timed("requant_x_colwise", lambda: om.requant_colwise(xq, xs, splits))
+    dyq, dys = timed("quantize_dy_rowwise", lambda: om.quantize_rowwise(dy))
+    timed("dgrad", lambda: og.dgrad(dyq, dys, wcq, wcs, splits, g))
+    dycq, dycs = timed("requant_dy_colwise", lambda: om.requant_colwise(dyq, dys, splits))
+    timed("dbias", lambda: om.grouped_dbias(dyq, dys, splits))
+    timed("wgrad", lambda: og.wgrad(dycq, dycs, xcq, xcs, splits))
+    dt = sum(ops.values())
     flops = 3 * 2.0 * rows * n_cols * k
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(threads, cores)),
             "kind": "oracle",
             "sample": f"{WORKLOAD}: first {rows} tokens as {g} experts x {rows // g}, "
                       f"{n_cols} of {w.ffn} output features, K={k}; every step of the path; "
-                      f"{dt:.2f} s wall, float64 NumPy"}
+                      f"{dt:.2f} s wall, float64 NumPy",
+            "affinity_cores": cores,
+            "blas": {"library": blas[0].get("internal_api") if blas else None,
+                     "version": blas[0].get("version") if blas else None,
+                     "threads": int(threads)},
+            "seconds_per_op": ops,
+            "note": "GEMMs use the multithreaded BLAS; quantize and requantize are vectorized "
+                    "NumPy on one thread; `cores` = the threads the BLAS used, bounded by the "
+                    "affinity mask"}
 
 
 def _time_outside(fn, steps):
@@ -376,10 +404,228 @@ def bench_group_quantize(steps, warmup):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+OTHERS = {}   # filled below: name -> bench function of the other workloads
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries: the tables under profiles/ are written by these from the
+# CSV output of the commands they quote (python bench.py --summarize ...).
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short_kernel(name):
+    """'void mx::quant_rowcol_kernel<true>(...)' -> 'quant_rowcol_kernel<true>'."""
+    n = name.replace("void ", "")
+    n = n.split("(")[0]
+    return n.replace("mx::", "")
+
+
+def _labels(names):
+    """Launch labels in dispatch order: the grouped GEMM's instantiations by
+    layout (<false, *, false> alternates forward and dgrad, as every step
+    launches them in that order), every other kernel by its short name."""
+    out, mgrouped = [], {}
+    for n in names:
+        k = _short_kernel(n)
+        if k.startswith("grouped_gemm_kernel<"):
+            targs = [a.strip() for a in k[k.index("<") + 1:k.rindex(">")].split(",")]
+            kg, bf, acc = (a == "true" for a in targs)
+            dt = "_bf16" if bf else ""
+            if acc:
+                out.append("wgrad_accumulate_TN")
+            elif kg:
+                out.append("wgrad_TN" + dt)
+            else:
+                i = mgrouped.get(dt, 0)
+                mgrouped[dt] = i + 1
+                out.append(("forward_NT" if i % 2 == 0 else "dgrad_NN") + dt)
+        else:
+            out.append(k)
+    return out
+
+
+def algorithmic_bytes(workload):
+    """Algorithmic HBM bytes per launch of each kernel of a workload's step:
+    codes and scales (1/32 of the codes) read or written once, fp32 outputs
+    and partials once."""
+    from moe_expert_grouped_group_amd import workloads as wl
+    sc = 1 + 1 / 32
+    if workload == "group_quantize_131072x7168":
+        t, k = 131072, 7168
+        return {"quant_rowcol_kernel": t * k * (2 + 2 * sc)}
+    g, t = len(wl.splits_for(workload)), int(wl.splits_for(workload).sum())
+    k, n = {"moe8_h4096_f14336": (4096, 14336)}[workload]
+    return {
+        "forward_NT": t * k * sc + g * n * k * sc + t * n * 4,
+        "dgrad_NN": t * n * sc + g * n * k * sc + t * k * 4,
+        "wgrad_TN": t * n * sc + t * k * sc + g * n * k * 4,
+        "wgrad_accumulate_TN": t * n * sc + t * k * sc + 2 * g * n * k * 4,
+        "quant_row_requant_kernel<false>": t * k * (2 + 2 * sc),
+        "quant_row_requant_kernel<true>": t * n * (2 + 2 * sc) + (t // 128) * n * 4,
+        "quant_rowcol_kernel": g * n * k * (2 + 2 * sc),
+        "dbias_finalize_kernel": (t // 128) * n * 4 + g * n * 4,
+    }
+
+
+def _counter_means(path):
+    """Mean counter value and duration (us) per launch label of a --pmc CSV."""
+    import collections
+    rows = _csv(path)
+    labels = _labels([r["Kernel_Name"] for r in rows])
+    vals, durs = collections.defaultdict(list), collections.defaultdict(list)
+    for r, lab in zip(rows, labels):
+        vals[lab].append(float(r["Counter_Value"]))
+        durs[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return ({k: sum(v) / len(v) for k, v in vals.items()},
+            {k: len(v) for k, v in vals.items()},
+            {k: sum(v) / len(v) for k, v in durs.items()})
+
+
+def summarize_traffic(workload, cal_fetch, cal_write, fetch, write, title, commands):
+    """Markdown + JSON of HBM bytes per launch from FETCH_SIZE and WRITE_SIZE
+    runs, scaled by the same counters on the 1 GiB copy of --calibrate-copy."""
+    cf, _, _ = _counter_means(os.path.join(cal_fetch, "p_counter_collection.csv"))
+    cw, _, _ = _counter_means(os.path.join(cal_write, "p_counter_collection.csv"))
+    copy = [k for k in cf if "copyBuffer" in k][0]
+    ff = round(COPY_BYTES / 1024 / cf[copy], 4)
+    fw = round(COPY_BYTES / 1024 / cw[copy], 4)
+    f, nf, df = _counter_means(os.path.join(fetch, "p_counter_collection.csv"))
+    w, _, _ = _counter_means(os.path.join(write, "p_counter_collection.csv"))
+    alg = algorithmic_bytes(workload)
+    per, tab = {}, []
+    for lab in sorted(f, key=lambda x: (x not in alg, x)):
+        if lab not in w:
+            continue
+        rd, wr = f[lab] * 1024 * ff, w[lab] * 1024 * fw
+        a = alg.get(lab)
+        per[lab] = {"fetch_kib": round(f[lab], 1), "write_kib": round(w[lab], 1),
+                    "read_bytes": int(rd), "write_bytes": int(wr), "hbm_bytes": int(rd + wr),
+                    "algorithmic_bytes": None if a is None else int(a), "launches": nf[lab],
+                    "us_under_counters": round(df[lab], 1)}
+        tab.append(f"| {lab} | {nf[lab]} | {f[lab]:.0f} | {w[lab]:.0f} | {rd / 1e9:.3f} | "
+                   f"{wr / 1e9:.3f} | " + (f"{a / 1e9:.3f} | {(rd + wr) / a:.2f}" if a else "- | -")
+                   + f" | {df[lab]:.1f} |")
+    step3 = [per[x]["hbm_bytes"] for x in ("forward_NT", "dgrad_NN", "wgrad_TN") if x in per]
+    rec = {"workload": workload, "source_sha256": gemm_source_hash(),
+           "quantize_source_sha256": quantize_source_hash(),
+           "copy_fetch_factor": ff, "copy_write_factor": fw, "per_launch": per}
+    if len(step3) == 3:
+        rec["hbm_bytes_per_launch"] = int(sum(step3) / 3)
+    cmd = "\n".join(commands)
+    md = f"""# {title}
+
+Counters, each in a run of its own (from the repository root, one MI355X):
+
+```
+{cmd}
+```
+
+Calibration: the 1 GiB device copy of `bench.py --calibrate-copy` reads {cf[copy]:.0f} KiB by FETCH_SIZE and writes {cw[copy]:.0f} KiB by WRITE_SIZE per copy, so the counters are scaled by {ff} (fetch) and {fw} (write).
+
+| launch | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | written GB (scaled) | algorithmic GB | ratio | us per launch under counters |
+|---|---|---|---|---|---|---|---|---|
+""" + "\n".join(tab) + f"""
+
+Algorithmic bytes: codes and E8M0 scales read or written once, fp32 outputs and partial sums once (the accumulating wgrad also reads its output).  FETCH_SIZE counts reads from L2 to the memory fabric (Infinity Cache hits included), so a ratio above 1 is re-fetch of data that fell out of L2, or partial lines written back piecemeal.  Durations under counter collection are longer than bench.py's event times.  Written by `python bench.py --summarize traffic ...` from the runs above.
+
+```json
+{json.dumps(rec, indent=1)}
+```
+"""
+    return md
+
+
+def summarize_trace(trace_dir, title, commands, note=""):
+    """Markdown table of a --kernel-trace run: per launch label (the GEMM by
+    layout, in dispatch order), calls, mean / min / max duration and total."""
+    import collections
+    path = [os.path.join(trace_dir, x) for x in os.listdir(trace_dir)
+            if x.endswith("kernel_trace.csv")][0]
+    rows = _csv(path)
+    labels = _labels([r["Kernel_Name"] for r in rows])
+    d = collections.defaultdict(list)
+    for r, lab in zip(rows, labels):
+        d[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in d.values())
+    tab = ["| launch | calls | avg us | median us | min us | max us | total ms | % |",
+           "|---|---|---|---|---|---|---|---|"]
+    for lab, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        sv = sorted(v)
+        tab.append(f"| `{lab}` | {len(v)} | {sum(v) / len(v):.1f} | {sv[len(sv) // 2]:.1f} | "
+                   f"{sv[0]:.1f} | {sv[-1]:.1f} | {sum(v) / 1e3:.3f} | "
+                   f"{100 * sum(v) / total:.1f} |")
+    cmd = "\n".join(commands)
+    return f"""# {title}
+
+Command (from the repository root, one MI355X):
+
+```
+{cmd}
+```
+
+From `{os.path.basename(path)}`, one row per launch label: the grouped GEMM's forward (`forward_NT`) and dgrad (`dgrad_NN`) are the two launches of `grouped_gemm_kernel<false, *, false>` in dispatch order, `wgrad_TN` is `<true, *, false>`, `wgrad_accumulate_TN` is `<true, false, true>`; a `_bf16` suffix marks bf16 outputs.  Written by `python bench.py --summarize trace ...`.
+
+""" + "\n".join(tab) + ("\n\n" + note if note else "") + "\n"
+
+
+def quantize_source_hash():
+    h = hashlib.sha256()
+    for rel in ["moe_expert_grouped_group_amd/csrc/quantize.hip",
+                "moe_expert_grouped_group_amd/csrc/mx_device.h",
+                "moe_expert_grouped_group_amd/csrc/mx_convert.h"]:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
+    return h.hexdigest()
+
+
+def summarize_main(argv):
+    ap = argparse.ArgumentParser(prog="bench.py --summarize")
+    ap.add_argument("kind", choices=["trace", "traffic"])
+    ap.add_argument("--out", required=True, help="markdown file to write")
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--command", action="append", default=[],
+                    help="the rocprofv3 command line(s) the CSVs came from (quoted in the file)")
+    ap.add_argument("--dir", help="trace: the rocprofv3 output directory")
+    ap.add_argument("--note", default="")
+    ap.add_argument("--workload", help="traffic: workload of the algorithmic bytes")
+    ap.add_argument("--cal-fetch")
+    ap.add_argument("--cal-write")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    a = ap.parse_args(argv)
+    if a.kind == "trace":
+        md = summarize_trace(a.dir, a.title, a.command, a.note)
+    else:
+        md = summarize_traffic(a.workload, a.cal_fetch, a.cal_write, a.fetch, a.write, a.title,
+                               a.command)
+    with open(a.out, "w") as f:
+        f.write(md)
+    print(md)
+
+
+OTHERS.update({"skewed_dsv3": bench_skewed_linear, "nemotron_proxy_mlp": bench_fused_mlp,
+               "group_quantize_131072x7168": bench_group_quantize})
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        summarize_main(sys.argv[2:])
+        return
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({args.only: OTHERS[args.only](args.steps, args.warmup)}), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MXFP8 grouped-GEMM "
@@ -501,10 +747,14 @@ def main():
         wall = time.perf_counter() - wall0
         ms_step = start.elapsed_time(stop) / args.steps
 
+    if args.step_only:
+        args.no_others = args.no_cpu = True
     # Outside the step: wgrad accumulated into an fp32 main_grad (the
     # production form of the wgrad launch), timed on the same operands.
-    acc_ms = None
-    if out_dtype == torch.float32:
+    acc_ms = sb_ms = sw_ms = sw_chain_ms = None
+    sb_bytes = sw_bytes = 0
+    sw_t, sw_f = 83968, 1024
+    if out_dtype == torch.float32 and not args.step_only:
         main_grad = torch.zeros(g, n, k, dtype=torch.float32, device=dev)
         acc = lambda: mx.grouped_gemm_wgrad_accumulate(  # noqa: E731
             dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t, n, k, main_grad,
@@ -514,33 +764,34 @@ def main():
 
     # Outside the step: gradients of a routing-scaled bias (dbias weighted by
     # each token's scale, and each token's scale gradient) from row-wise dY.
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(7)
-    r_scales = torch.rand(t, device=dev, generator=gen)
-    r_bias = torch.randn(g, n, device=dev, generator=gen)
-    sb_ws = torch.empty(mx.load_library().mxfp8_scaled_bias_workspace_bytes(t, n), **u8)
-    sb_ms = _time_outside(lambda: mx.grouped_scaled_bias_grad(
-        dyo.row_data, dyo.row_scale, ms, r_scales, r_bias, workspace=sb_ws), args.steps)
-    # dY codes and scales read once, scales and bias read, both partial sums
-    # written and read back, both outputs written
-    sb_bytes = (t * n * (1 + 1 / 32) + t * 4 + g * n * 4 + 2 * (t // 128) * n * 4
-                + 2 * t * (n // 512) * 4 + g * n * 4 + t * 4)
-    # Outside the step: the fused expert MLP's activation (SwiGLU of the FC1
-    # output, quantized row- and column-wise for FC2) at the Nemotron-proxy
-    # MLP shape (T = 83968 tokens, FC1 out 2F = 2048), fused in one kernel and
-    # as the two-kernel chain it replaces.
-    sw_t, sw_f = 83968, 1024
-    hgen = torch.Generator(device=dev)
-    hgen.manual_seed(11)
-    h_sw = (torch.randn(sw_t, 2 * sw_f, device=dev, generator=hgen) * 3).to(torch.bfloat16)
-    sw_out = mx.swiglu_quantize(h_sw)
-    a_sw = mx.swiglu_fwd(h_sw)
-    sw_ms = _time_outside(lambda: mx.swiglu_quantize(h_sw, out=sw_out), args.steps)
-    sw_chain_ms = _time_outside(lambda: mx.group_quantize(
-        mx.swiglu_fwd(h_sw, out=a_sw), mx.ROWWISE | mx.COLWISE, out=sw_out), args.steps)
-    # fused: h read (4 B per output element), row + column copies written
-    sw_bytes = sw_t * sw_f * (4 + 2 * (1 + 1 / 32))
-    del h_sw, sw_out, a_sw
+    if not args.step_only:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        r_scales = torch.rand(t, device=dev, generator=gen)
+        r_bias = torch.randn(g, n, device=dev, generator=gen)
+        sb_ws = torch.empty(mx.load_library().mxfp8_scaled_bias_workspace_bytes(t, n), **u8)
+        sb_ms = _time_outside(lambda: mx.grouped_scaled_bias_grad(
+            dyo.row_data, dyo.row_scale, ms, r_scales, r_bias, workspace=sb_ws), args.steps)
+        # dY codes and scales read once, scales and bias read, both partial
+        # sums written and read back, both outputs written
+        sb_bytes = (t * n * (1 + 1 / 32) + t * 4 + g * n * 4 + 2 * (t // 128) * n * 4
+                    + 2 * t * (n // 512) * 4 + g * n * 4 + t * 4)
+        del r_scales, r_bias, sb_ws
+        # Outside the step: the fused expert MLP's activation (SwiGLU of the
+        # FC1 output, quantized row- and column-wise for FC2) at the
+        # Nemotron-proxy MLP shape (T = 83968 tokens, FC1 out 2F = 2048),
+        # fused in one kernel and as the two-kernel chain it replaces.
+        hgen = torch.Generator(device=dev)
+        hgen.manual_seed(11)
+        h_sw = (torch.randn(sw_t, 2 * sw_f, device=dev, generator=hgen) * 3).to(torch.bfloat16)
+        sw_out = mx.swiglu_quantize(h_sw)
+        a_sw = mx.swiglu_fwd(h_sw)
+        sw_ms = _time_outside(lambda: mx.swiglu_quantize(h_sw, out=sw_out), args.steps)
+        sw_chain_ms = _time_outside(lambda: mx.group_quantize(
+            mx.swiglu_fwd(h_sw, out=a_sw), mx.ROWWISE | mx.COLWISE, out=sw_out), args.steps)
+        # fused: h read (4 B per output element), row + column copies written
+        sw_bytes = sw_t * sw_f * (4 + 2 * (1 + 1 / 32))
+        del h_sw, sw_out, a_sw
 
     flop_one = 2.0 * t * n * k
     gemm_ms = per["gemm_fprop"] + per["gemm_dgrad"] + per["gemm_wgrad"]
@@ -579,15 +830,15 @@ def main():
         "wgrad_accumulate": None if acc_ms is None else {
             "ms": round(acc_ms, 4), "tflops": round(flop_one / (acc_ms * 1e-3) / 1e12, 2),
             "note": "main_grad += dY^T X in fp32, outside the step"},
-        "scaled_bias_grad": {"ms": round(sb_ms, 4),
-                             "gbs": round(sb_bytes / (sb_ms * 1e-3) / 1e9, 1),
-                             "note": "dbias and dscales of a routing-scaled bias from row-wise "
-                                     "dY, outside the step"},
-        "swiglu_quantize": {"ms": round(sw_ms, 4),
-                            "gbs": round(sw_bytes / (sw_ms * 1e-3) / 1e9, 1),
-                            "unfused_ms": round(sw_chain_ms, 4),
-                            "note": f"SwiGLU + row/col MXFP8 of h [{sw_t}, {2 * sw_f}] in one "
-                                    "kernel vs swiglu_fwd + group_quantize, outside the step"},
+        "scaled_bias_grad": None if sb_ms is None else {
+            "ms": round(sb_ms, 4), "gbs": round(sb_bytes / (sb_ms * 1e-3) / 1e9, 1),
+            "note": "dbias and dscales of a routing-scaled bias from row-wise dY, outside the "
+                    "step"},
+        "swiglu_quantize": None if sw_ms is None else {
+            "ms": round(sw_ms, 4), "gbs": round(sw_bytes / (sw_ms * 1e-3) / 1e9, 1),
+            "unfused_ms": round(sw_chain_ms, 4),
+            "note": f"SwiGLU + row/col MXFP8 of h [{sw_t}, {2 * sw_f}] in one kernel vs "
+                    "swiglu_fwd + group_quantize, outside the step"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),
@@ -601,13 +852,11 @@ def main():
     if not args.no_others:
         # the other workloads, each timed the same way (fewer steps), outside
         # the headline step
-        del x, wt, dy, xo, wo, xc, dyo, dyc, y, dx, dw, db, ws, r_scales, r_bias, sb_ws
+        del x, wt, dy, xo, wo, xc, dyo, dyc, y, dx, dw, db, ws
         torch.cuda.empty_cache()
         o_steps, o_warm = max(3, min(args.steps, 10)), max(1, min(args.warmup, 2))
         others = {}
-        for name, fn in (("skewed_dsv3", bench_skewed_linear),
-                         ("nemotron_proxy_mlp", bench_fused_mlp),
-                         ("group_quantize_131072x7168", bench_group_quantize)):
+        for name, fn in OTHERS.items():
             others[name] = fn(o_steps, o_warm)
             torch.cuda.empty_cache()
         res["other_workloads"] = others

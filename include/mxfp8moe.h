@@ -25,6 +25,11 @@
  *    transposed: bytes [C, R] and scales [C, R/32], both row-major.  It is the
  *    copy the wgrad GEMM reads ([P3244] Greptile Summary flowchart;
  *    [P3545] Description: every wgrad path takes the column-wise tiles).
+ *  - bf16 inputs must be finite.  Neither the pages nor the OCP rule give a
+ *    scale for a block that holds Inf or NaN; the bytes written for such a
+ *    block are unspecified (they are not NaN-propagating), and there the
+ *    fused mxfp8_group_quantize_requant may differ from the separate
+ *    quantize and requantize calls.  No entry point checks for this.
  *  - Scale arrays have exactly the shape (T, K/32): the page's padded shape
  *    (round_up(T,128), round_up(K/32,4)) ([P3244] review thread on
  *    scale_shape) has no padding under the alignment contract below.
@@ -159,7 +164,8 @@ mxfp8_status mxfp8_requant_colwise(const uint8_t* q_row, const uint8_t* s_row, i
  *  x: bf16 [T, K]; q_row/s_row: [T, K] + [T, K/32]; q_col/s_col: the
  *  transposed column-wise copy [K, T] + [K, T/32]; dbias, m_splits, G,
  *  workspace as for mxfp8_requant_colwise.
- *  Every output byte (and dbias, bit for bit) equals what the two calls give.
+ *  For finite x every output byte (and dbias, bit for bit) equals what the
+ *  two calls give.
  * Errors: EINVAL for NULL pointers (T > 0), T % 128, K % 512, and as
  * mxfp8_requant_colwise for dbias.
  */

@@ -84,3 +84,41 @@ def random_mx(rng, rows, cols, smin=112, smax=142):
     q[(q & 0x7F) == 0x7F] = 0x7E
     s = rng.integers(smin, smax + 1, size=(rows, cols // 32)).astype(np.uint8)
     return q, s
+
+
+def tol_report(tag, got, ref, mag, out_dtype_is_f32, win=None):
+    """Record how far a GEMM output sits from the stated bound.
+
+    fp32: the worst |gpu - oracle| / (1e-5 * sum|ab| + 1e-6), and the same
+    against the MFMA window bound when `win` is given.  bf16: the worst
+    |gpu - bf16(oracle)| in units of one bf16 ulp of bf16(oracle), and the
+    count of outputs beyond one ulp.  Printed, and appended as a JSON line to
+    the file named by MX_TOL_REPORT when that variable is set.
+    """
+    import json
+    import os
+
+    from oracle import gemm as og
+    from oracle import mxfp8 as om
+
+    got = np.asarray(got, dtype=np.float64)
+    rec = {"case": tag, "n": int(got.size)}
+    if out_dtype_is_f32:
+        err = np.abs(got - ref)
+        rec["max_err_over_f32_bound"] = float((err / og.tolerance_f32(mag)).max())
+        rec["n_over_f32_bound"] = int((err > og.tolerance_f32(mag)).sum())
+        if win is not None:
+            rec["max_err_over_mfma_bound"] = float((err / og.tolerance_mfma(mag, win)).max())
+    else:
+        r16 = om.round_to_bf16(ref)
+        ulps = np.abs(got - r16) / om.bf16_ulp(r16)
+        rec["max_err_in_bf16_ulp"] = float(ulps.max())
+        rec["n_over_1_ulp"] = int((ulps > 1).sum())
+        rec["max_err_over_ulp_plus_f32_bound"] = float(
+            (np.abs(got - r16) / (om.bf16_ulp(r16) + og.tolerance_f32(mag))).max())
+    log("TOL " + json.dumps(rec))
+    path = os.environ.get("MX_TOL_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return rec

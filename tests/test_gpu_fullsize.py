@@ -1,7 +1,8 @@
 """Full-size parity of the hot path on the workloads of the benchmark table,
-in the launch configuration bench.py times (the same kernels and grids over
-the same sizes), checked on sampled outputs that the oracle computes one by
-one from the original bf16 inputs.
+with the calls and launch configuration bench.py times (the fused quantize +
+requantize of X and dY with dbias, the wgrad through the tile counter, the
+same grids over the same sizes), checked on sampled outputs that the oracle
+computes one by one from the original bf16 inputs.
 
 Sampling (seeded): 128-row windows at the start of two experts for the
 forward and dgrad outputs (all the window's rows, 64 sampled columns); two
@@ -10,11 +11,18 @@ forward and dgrad outputs (all the window's rows, 64 sampled columns); two
 quantizes only what a sample needs: a window's rows, a 32-wide block of
 columns (a 1 x 32 block never crosses it), or one column of the weights for
 the column-wise weight copy.  Byte outputs are compared bit-exactly; GEMM
-outputs with the bounds of oracle.gemm (tolerance_f32 for forward and dgrad
-on Gaussian data, tolerance_mfma for wgrad and outlier data, bf16 within one
-ulp widened by the same allowance).  Properties that hold at any size are
-checked on whole outputs: a zero weight gradient for every expert without
-tokens.
+outputs with the bounds of oracle.gemm: tolerance_f32 (the stated 1e-5 rule)
+for every GEMM on Gaussian data, bf16 within one ulp widened by it;
+tolerance_mfma only for the outlier workload and the FC2 wgrad of the MLP,
+whose outputs exceed the stated rule (each check records its worst ratio to
+the stated rule through gpu_util.tol_report).
+
+Properties that hold at any size are checked on whole outputs: the fused
+quantize + requantize equals the two separate calls byte for byte (dbias bit
+for bit); the wgrad through the tile counter equals the fixed order byte for
+byte; the accumulating wgrad (with and without the counter) equals main_grad
++ the plain wgrad, bit for bit; a zero weight gradient for every expert
+without tokens.
 """
 
 import numpy as np
@@ -27,7 +35,7 @@ from oracle import gemm as og
 from oracle import mxfp8 as om
 from oracle import swiglu as osw
 
-from gpu_util import dev, f64, log, u8
+from gpu_util import dev, f64, log, tol_report, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +45,9 @@ def _bf(t):
     return t.float().numpy().astype(np.float64)
 
 
-def _check(got, ref, mag, out_dtype, win=None):
+def _check(got, ref, mag, out_dtype, win=None, tag=None):
+    if tag is not None:
+        tol_report(tag, got, ref, mag, out_dtype == torch.float32, win)
     tol = og.tolerance_f32(mag) if win is None else og.tolerance_mfma(mag, win)
     if out_dtype == torch.float32:
         err = np.abs(got - ref)
@@ -46,6 +56,10 @@ def _check(got, ref, mag, out_dtype, win=None):
     else:
         ok = og.within_bf16_ulp(got, ref, tol)
         assert ok.all(), int((~ok).sum())
+
+
+def _same_bytes(a, b, what):
+    assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), what
 
 
 def _offsets(splits):
@@ -61,27 +75,81 @@ def _window_experts(splits, rng):
 
 
 def _run_linear(w, out_dtype):
-    """The hot path of one expert linear on the GPU, as bench.py runs it."""
+    """The hot path of one expert linear on the GPU, with bench.py's calls.
+
+    X: the fused row-wise quantize + column-wise requantize (the skewed
+    workload's X arrives quantized, so there it is quantized row-wise and
+    requantized, as bench.py does); W: row + column-wise quantize; dY: the
+    fused quantize + requantize with dbias; wgrad through the tile counter.
+    The same tensors are also produced by the separate calls (quantize, then
+    requantize; the wgrad in the fixed order) and compared byte for byte on
+    whole tensors; with fp32 outputs the accumulating wgrad (with and without
+    the counter) is compared with main_grad + the plain wgrad, bit for bit.
+    """
     g, t, k, n = w.groups, w.tokens, w.hidden, w.ffn
     ms = dev(w.m_splits)
     x = w.tensors["x"].to("cuda")
     wt = w.tensors["w"].to("cuda")
     dy = w.dy.to("cuda")
+    u8_ = dict(dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mx.dbias_workspace_bytes(t, n), **u8_)
+    gws = torch.empty(mx.gemm_workspace_bytes(), **u8_)
     log(f"full-size {w.name}: quantize")
-    xo = mx.group_quantize(x, mx.ROWWISE)
+    if w.name == "skewed_dsv3":
+        xo = mx.group_quantize(x, mx.ROWWISE)
+        xc = mx.requant_colwise(xo.row_data, xo.row_scale)
+    else:
+        xo = mx.group_quantize_requant(x)
+        xc = xo
     wo = mx.group_quantize(wt, mx.ROWWISE | mx.COLWISE)
     log(f"full-size {w.name}: forward")
     y = mx.grouped_gemm("NT", xo.row_data, xo.row_scale, wo.row_data, wo.row_scale, ms, t, n, k,
                         out_dtype)
-    xc = mx.requant_colwise(xo.row_data, xo.row_scale)
     log(f"full-size {w.name}: backward")
-    dyo = mx.group_quantize(dy, mx.ROWWISE)
-    dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True)
+    dyo, db = mx.group_quantize_requant(dy, ms, with_dbias=True, workspace=ws)
+    dyc = dyo
     dx = mx.grouped_gemm("NN", dyo.row_data, dyo.row_scale, wo.col_data, wo.col_scale, ms, t, n,
                          k, out_dtype)
     dw = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t,
-                         n, k, out_dtype)
+                         n, k, out_dtype, workspace=gws)
     torch.cuda.synchronize()
+
+    log(f"full-size {w.name}: separate calls and fixed wgrad order, byte for byte")
+    xo2 = mx.group_quantize(x, mx.ROWWISE)
+    xc2 = mx.requant_colwise(xo2.row_data, xo2.row_scale)
+    dyo2 = mx.group_quantize(dy, mx.ROWWISE)
+    dyc2, db2 = mx.requant_colwise(dyo2.row_data, dyo2.row_scale, ms, with_dbias=True)
+    torch.cuda.synchronize()
+    for part in ("row_data", "row_scale"):
+        _same_bytes(getattr(xo, part), getattr(xo2, part), f"X {part}")
+        _same_bytes(getattr(dyo, part), getattr(dyo2, part), f"dY {part}")
+    for part in ("col_data", "col_scale"):
+        _same_bytes(getattr(xc, part), getattr(xc2, part), f"X {part}")
+        _same_bytes(getattr(dyc, part), getattr(dyc2, part), f"dY {part}")
+    _same_bytes(db, db2, "dbias")
+    del xo2, xc2, dyo2, dyc2, db2
+    dw2 = mx.grouped_gemm("TN", dyc.col_data, dyc.col_scale, xc.col_data, xc.col_scale, ms, t,
+                          n, k, out_dtype)
+    torch.cuda.synchronize()
+    _same_bytes(dw, dw2, "wgrad: tile counter vs fixed order")
+    del dw2
+    if out_dtype == torch.float32:
+        log(f"full-size {w.name}: accumulating wgrad")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(31)
+        base = torch.randn(g, n, k, device="cuda", generator=gen)
+        base[torch.from_numpy(w.m_splits == 0).cuda()] = -0.0
+        for wsp in (gws, None):
+            mg = base.clone()
+            mx.grouped_gemm_wgrad_accumulate(dyc.col_data, dyc.col_scale, xc.col_data,
+                                             xc.col_scale, ms, t, n, k, mg, workspace=wsp)
+            torch.cuda.synchronize()
+            ref = base + dw
+            empty = torch.from_numpy(w.m_splits == 0).cuda()
+            ref[empty] = base[empty]    # untouched, signed zeros included
+            _same_bytes(mg, ref, f"accumulate (workspace={wsp is not None})")
+            del mg, ref
+        del base
     del x, wt, dy
     return dict(xo=xo, wo=wo, y=y, xc=xc, dyo=dyo, dyc=dyc, db=db, dx=dx, dw=dw)
 
@@ -106,7 +174,7 @@ def _check_linear(w, r, out_dtype, outliers, seed):
         ref, mag, win = og.fprop(xq, xs, wq[None], ws[None], [128], True, True)
         log(f"full-size {w.name}: forward rows of expert {e}")
         _check(f64(r["y"][rows][:, torch.from_numpy(cols).cuda()]), ref, mag, out_dtype,
-               win if outliers else None)
+               win if outliers else None, tag=f"{w.name} forward expert {e}")
 
         dyq, dys = om.quantize_rowwise(_bf(dy_t[rows]))
         assert np.array_equal(u8(r["dyo"].row_data[rows]), dyq), f"dY rows of expert {e}"
@@ -118,7 +186,8 @@ def _check_linear(w, r, out_dtype, outliers, seed):
         assert np.array_equal(u8(r["wo"].col_scale[torch.from_numpy(kcols).cuda()]), wcs)
         ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, one, g, True)
         log(f"full-size {w.name}: dgrad rows of expert {e}")
-        _check(f64(r["dx"][rows][:, torch.from_numpy(kcols).cuda()]), ref2, mag2, out_dtype)
+        _check(f64(r["dx"][rows][:, torch.from_numpy(kcols).cuda()]), ref2, mag2, out_dtype,
+               tag=f"{w.name} dgrad expert {e}")
 
     # column-wise copies and dbias on two 32-wide column blocks (all tokens)
     kb = np.sort(rng.choice(k // 32, size=2, replace=False))
@@ -151,7 +220,12 @@ def _check_linear(w, r, out_dtype, outliers, seed):
     nsel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in nb])).cuda()
     ksel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in kb])).cuda()
     log(f"full-size {w.name}: wgrad samples")
-    _check(f64(r["dw"][:, nsel][:, :, ksel]), ref3, mag3, out_dtype, win3)
+    # Gate: the stated 1e-5 rule (bf16: one ulp plus it) where the sampled
+    # outputs meet it (worst ratios on these seeds: 0.70 for the 8-expert
+    # bench, 0.99 for the MLP's FC1); the MFMA window bound only for the
+    # outlier workload, whose wgrad exceeds the stated rule 47-fold.
+    _check(f64(r["dw"][:, nsel][:, :, ksel]), ref3, mag3, out_dtype,
+           win3 if outliers else None, tag=f"{w.name} wgrad")
     for gi, m in enumerate(splits):
         if m == 0:
             assert torch.count_nonzero(r["dw"][gi]).item() == 0, f"expert {gi} has no tokens"
@@ -277,7 +351,8 @@ def test_fullsize_fused_mlp_fc2_and_swiglu():
         ref, mag, wn = og.fprop(u8(ao.row_data[win]), u8(ao.row_scale[win]), wq[None], wsc[None],
                                 [128], True, True)
         log(f"full-size {name}: FC2 forward rows of expert {e}")
-        _check(f64(y[win][:, torch.from_numpy(cols).cuda()]), ref, mag, bf, wn)
+        _check(f64(y[win][:, torch.from_numpy(cols).cuda()]), ref, mag, bf, wn,
+               tag=f"{name} FC2 forward expert {e}")
         # FC2 dgrad: dOut rows (oracle quantize) times the column-wise W2 copy
         dyq, dys = om.quantize_rowwise(_bf(dy_t[win]))
         assert np.array_equal(u8(dyo.row_data[win]), dyq)
@@ -288,7 +363,8 @@ def test_fullsize_fused_mlp_fc2_and_swiglu():
         one = [128 if gi == e else 0 for gi in range(g)]
         ref2, mag2 = og.dgrad(dyq, dys, wcq, wcs, one, g, True)
         log(f"full-size {name}: FC2 dgrad rows of expert {e}")
-        _check(f64(da[win][:, torch.from_numpy(fcols).cuda()]), ref2, mag2, bf)
+        _check(f64(da[win][:, torch.from_numpy(fcols).cuda()]), ref2, mag2, bf,
+               tag=f"{name} FC2 dgrad expert {e}")
         # SwiGLU backward on the GPU's h and da rows
         assert og.within_bf16_ulp(f64(dh[win]), osw.swiglu_bwd(f64(h[win]), f64(da[win]))).all()
 
@@ -310,7 +386,10 @@ def test_fullsize_fused_mlp_fc2_and_swiglu():
     ksel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in kb])).cuda()
     fsel = torch.from_numpy(np.concatenate([np.arange(b * 32, b * 32 + 32) for b in fb])).cuda()
     log(f"full-size {name}: FC2 wgrad samples")
-    _check(f64(dw2[:, ksel][:, :, fsel]), ref3, mag3, bf, win3)
+    # the FC2 wgrad contracts SwiGLU outputs (windows that mix near-zero and
+    # large activations): 1.67 times one ulp plus the 1e-5 rule at worst, so
+    # it keeps the MFMA window bound
+    _check(f64(dw2[:, ksel][:, :, fsel]), ref3, mag3, bf, win3, tag=f"{name} FC2 wgrad")
     for gi, m in enumerate(splits):
         if m == 0:
             assert torch.count_nonzero(dw2[gi]).item() == 0, f"expert {gi} has no tokens"

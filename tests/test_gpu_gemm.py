@@ -146,20 +146,33 @@ def test_split_contraction_halves(kind, layout):
             _check(f64(out), ref, mag, torch.float32, win)
 
 
-@pytest.mark.parametrize("case", range(len(CASES) + 1))
+# wgrad tile-counter cases beyond CASES: most tokens on one expert of 24 (a
+# few long tiles beside many short ones), one empty expert, so the tiles go
+# through the counter; at N = K = 512 that is 96 tiles (fewer than the CUs),
+# at N = K = 2048 1536 tiles, several per workgroup, with 4 x 2 tile blocks
+# per expert (the accumulating wgrad's blocked order); then 8 experts, none
+# empty, 1024 tiles.
+COUNTER_CASES = [
+    ([0, 3072, 128, 256, 128] + [128] * 19, 1024, 512),
+    ([0, 3072, 128, 256, 128] + [128] * 19, 2048, 2048),
+    ([256, 896, 384, 128, 512, 640, 128, 256], 4096, 2048),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES) + len(COUNTER_CASES)))
 def test_wgrad_tile_counter_same_bytes(case):
     """The wgrad with a tile counter (mxfp8_grouped_gemm_ws: tiles handed out
     as workgroups finish) gives the same bytes as the fixed assignment, in
     fp32 and bf16 and accumulated into main_grad, twice with one workspace.
-    The extra case routes most tokens to one expert of 24 (a few long tiles
-    beside many short ones) with one empty expert: fewer than 1 in 8 experts
-    empty, so its tiles go through the counter; the other cases (1 in 4 or
-    more empty, or a single expert) cover the kernel's choice of the fixed
-    order despite a workspace."""
+    The COUNTER_CASES have fewer than 1 in 8 experts empty, so their tiles go
+    through the counter (the last two with several tiles per workgroup: the
+    counter's hand-out past the first round, and the accumulating wgrad's
+    blocked order); the CASES (1 in 4 or more empty, or a single expert)
+    cover the kernel's choice of the fixed order despite a workspace."""
     if case < len(CASES):
         splits, n, k = CASES[case]
     else:
-        splits, n, k = [0, 3072, 128, 256, 128] + [128] * 19, 1024, 512
+        splits, n, k = COUNTER_CASES[case - len(CASES)]
     g, t = len(splits), sum(splits)
     rng = np.random.default_rng(500 + case)
     aq, as_ = random_mx(rng, n, t)
@@ -167,7 +180,7 @@ def test_wgrad_tile_counter_same_bytes(case):
     ms = dev(np.asarray(splits, dtype=np.int64))
     ws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda")
     A, As, B, Bs = dev(aq), dev(as_), dev(bq), dev(bs)
-    log(f"gemm TN tile counter case {case}")
+    log(f"gemm TN tile counter case {case}: {g} experts, {t} tokens, N={n}, K={k}")
     for dt in (torch.float32, torch.bfloat16):
         ref = mx.grouped_gemm("TN", A, As, B, Bs, ms, t, n, k, dt)
         for _ in range(2):
@@ -180,6 +193,30 @@ def test_wgrad_tile_counter_same_bytes(case):
     mx.grouped_gemm_wgrad_accumulate(A, As, B, Bs, ms, t, n, k, m2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(m1.view(torch.uint8), m2.view(torch.uint8))
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_wgrad_accumulate_many_tiles_exact(use_ws):
+    """The accumulating wgrad where every workgroup takes several tiles (8
+    experts, none empty, 4096 x 2048 outputs: 1024 tiles of 256 x 256), in
+    the fixed order and through the tile counter (the blocked per-XCD order):
+    on integer-valued operands with unit scales and an integer main_grad every
+    fp32 sum is exact, so the result must equal the oracle exactly."""
+    splits, n, k = [256, 896, 384, 128, 512, 640, 128, 256], 4096, 2048
+    g, t = len(splits), sum(splits)
+    rng = np.random.default_rng(4242)
+    dycq, dycs = _mx_rows(rng, n, t, "integer")
+    xcq, xcs = _mx_rows(rng, k, t, "integer")
+    base = rng.integers(-64, 65, size=(g, n, k)).astype(np.float32)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    mg = dev(base)
+    ws = torch.empty(mx.gemm_workspace_bytes(), dtype=torch.uint8, device="cuda") if use_ws else None
+    log(f"wgrad accumulate, 1024 tiles, workspace={use_ws}")
+    mx.grouped_gemm_wgrad_accumulate(dev(dycq), dev(dycs), dev(xcq), dev(xcs), ms, t, n, k, mg,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    ref = og.wgrad_accumulate(base, dycq, dycs, xcq, xcs, splits)
+    assert np.array_equal(mg.cpu().numpy().astype(np.float64), ref)
 
 
 @pytest.mark.parametrize("kind", ["random", "integer"])

@@ -61,6 +61,11 @@ def _run_all(w, x, wt, dy, h, g):
     dyc, db = mx.requant_colwise(dyo.row_data, dyo.row_scale, ms, with_dbias=True,
                                  out=_mx(g, t, n, row=False), dbias=g((G, n), f32))
     db2 = mx.grouped_dbias(dyo.row_data, dyo.row_scale, ms, dbias=g((G, n), f32))
+    # the fused quantize + requantize (with dbias and its workspace guarded too)
+    xf = mx.group_quantize_requant(x, out=_mx(g, t, k))
+    dyf, dbf = mx.group_quantize_requant(
+        dy, ms, with_dbias=True, out=_mx(g, t, n), dbias=g((G, n), f32),
+        workspace=g((mx.dbias_workspace_bytes(t, n),), torch.uint8))
     sc = torch.linspace(0.5, 1.5, t, device="cuda")
     bias = torch.linspace(-1.0, 1.0, G * n, device="cuda").view(G, n)
     sdb, sds = mx.grouped_scaled_bias_grad(dyo.row_data, dyo.row_scale, ms, sc, bias,
@@ -83,12 +88,13 @@ def _run_all(w, x, wt, dy, h, g):
     dh = mx.swiglu_bwd(h, a, out=g((t, 2 * f), bf))
     ao = mx.swiglu_quantize(h, out=_mx(g, t, f))
     torch.cuda.synchronize()
-    for name, v in (("xo", xo), ("wo", wo), ("dyo", dyo), ("xc", xc), ("dyc", dyc), ("ao", ao)):
+    for name, v in (("xo", xo), ("wo", wo), ("dyo", dyo), ("xc", xc), ("dyc", dyc), ("ao", ao),
+                    ("xf", xf), ("dyf", dyf)):
         for part in ("row_data", "row_scale", "col_data", "col_scale"):
             if getattr(v, part) is not None:
                 out[f"{name}.{part}"] = getattr(v, part).clone()
-    for name, v in (("db", db), ("db2", db2), ("sdb", sdb), ("sds", sds), ("y", y), ("dx", dx),
-                    ("dw", dw), ("dw2", dw2), ("mg", mg), ("a", a), ("dh", dh)):
+    for name, v in (("db", db), ("db2", db2), ("dbf", dbf), ("sdb", sdb), ("sds", sds), ("y", y),
+                    ("dx", dx), ("dw", dw), ("dw2", dw2), ("mg", mg), ("a", a), ("dh", dh)):
         out[name] = v.clone()
     return out
 
@@ -96,10 +102,11 @@ def _run_all(w, x, wt, dy, h, g):
 @pytest.mark.parametrize("name", ["small_moe8", "small_skewed"])
 def test_guard_bands_and_run_twice(name):
     """No entry point writes outside its outputs (a canary margin on both
-    sides of every output stays intact, also around experts without tokens),
-    and a second run gives the same bytes (every reduction runs in a fixed
-    order; the wgrad's tile counter only changes which workgroup computes a
-    tile)."""
+    sides of every output, and of the fused quantize's dbias workspace, stays
+    intact, also around experts without tokens), and a second run gives the
+    same bytes (every reduction runs in a fixed order; the wgrad's tile
+    counter only changes which workgroup computes a tile).  The fused
+    quantize + requantize gives the bytes of the two separate calls."""
     w = wl.make(name)
     x, wt, dy = (w.tensors[nm].cuda() for nm in ("x", "w", "dy"))
     h = wl.bf16_normal([w.wid, wl.STREAM_DY, 77], (w.tokens, 1024)).cuda()
@@ -112,6 +119,14 @@ def test_guard_bands_and_run_twice(name):
     for key in runs[0]:
         a, b = runs[0][key], runs[1][key]
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), key
+    # the fused launches give the bytes of the separate quantize and requantize
+    r = runs[0]
+    for fused, row, col in (("xf", "xo", "xc"), ("dyf", "dyo", "dyc")):
+        for part in ("row_data", "row_scale"):
+            assert torch.equal(r[f"{fused}.{part}"], r[f"{row}.{part}"]), (fused, part)
+        for part in ("col_data", "col_scale"):
+            assert torch.equal(r[f"{fused}.{part}"], r[f"{col}.{part}"]), (fused, part)
+    assert torch.equal(r["dbf"].view(torch.uint8), r["db"].view(torch.uint8))
 
 
 @pytest.mark.parametrize("j", [-3, 5])

@@ -176,6 +176,34 @@ mxfp8_status mxfp8_group_quantize_requant(const uint16_t* x, int64_t T, int64_t 
                                           void* stream);
 
 /*
+ * mxfp8_group_quantize_requant_noalloc -- mxfp8_group_quantize_requant for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same work and
+ * the same bytes, with no workspace argument.  The dbias partial sums live in
+ * a static device array of MXFP8_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library (one per GPU, held until the process ends; its address is looked
+ * up on the first call on each device).  The call allocates and frees
+ * nothing.
+ *  Arguments as mxfp8_group_quantize_requant, without workspace.
+ *  Limit: with dbias, (T/128) * K * 4 bytes of partials must fit the array,
+ *  i.e. mxfp8_dbias_workspace_bytes(T, K) <= MXFP8_NOALLOC_SCRATCH_BYTES
+ *  (32 MiB: for K = 14336, T up to 74880; for K = 7168, up to 149760);
+ *  without dbias there is no limit.
+ *  Every call on one GPU shares that GPU's array, and the array keeps the
+ *  last call's partials: calls with dbias that may overlap on one GPU (on
+ *  different streams, or from different threads) race on it and give wrong
+ *  dbias.  Stream-ordered calls, graph replays included, are safe.  Nothing
+ *  needs clearing: each call writes every partial its finalize reads.
+ * Errors: as mxfp8_group_quantize_requant, and EINVAL when the partials of
+ * the requested dbias exceed the static array.
+ */
+#define MXFP8_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mxfp8_status mxfp8_group_quantize_requant_noalloc(const uint16_t* x, int64_t T, int64_t K,
+                                                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                                  uint8_t* s_col, const int64_t* m_splits,
+                                                  int32_t G, float* dbias, void* stream);
+
+/*
  * mxfp8_grouped_dbias -- grouped bias gradient from row-wise MXFP8 dY with no
  * column-wise copy (the frozen-weight case: [P3244] Greptile Summary, dbias
  * reduced without a wgrad stage).

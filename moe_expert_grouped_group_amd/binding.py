@@ -216,6 +216,35 @@ def group_quantize_requant(x, m_splits=None, with_dbias=False, out=None, dbias=N
     return (out, dbias) if with_dbias else out
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MXFP8_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def group_quantize_requant_noalloc(x, m_splits=None, with_dbias=False, out=None, dbias=None,
+                                   stream=None):
+    """group_quantize_requant without a workspace: the dbias partial sums go
+    to the library's static per-GPU scratch (mxfp8_group_quantize_requant_
+    noalloc; with dbias, (T/128) * K * 4 <= NOALLOC_SCRATCH_BYTES).  Calls
+    with dbias that overlap on one GPU race on that scratch.  Pass `out` (and
+    `dbias`) to keep the call free of allocations."""
+    lib = _lib()
+    t, k = x.shape
+    _need(x, torch.bfloat16, (t, k), "x")
+    out = _mx_outputs(out, ROWWISE | COLWISE, t, k, x)
+    g = 0
+    ms = None
+    if with_dbias:
+        ms = _splits(m_splits)
+        g = ms.numel()
+        if dbias is None:
+            dbias = _empty((g, k), torch.float32, x)
+        _need(dbias, torch.float32, (g, k), "dbias")
+    st = lib.mxfp8_group_quantize_requant_noalloc(
+        _ptr(x), t, k, _ptr(out.row_data), _ptr(out.row_scale), _ptr(out.col_data),
+        _ptr(out.col_scale), _ptr(ms), g, _ptr(dbias) if with_dbias else None, _stream(stream))
+    _native.check(st, "mxfp8_group_quantize_requant_noalloc")
+    return (out, dbias) if with_dbias else out
+
+
 def grouped_dbias(row_data, row_scale, m_splits, dbias=None, workspace=None, stream=None):
     """Row-wise MXFP8 dY [T, N] -> dbias [G, N] fp32 (sum over each expert's rows)."""
     lib = _lib()

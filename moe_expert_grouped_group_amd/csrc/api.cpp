@@ -150,6 +150,38 @@ mxfp8_status mxfp8_group_quantize_requant(const uint16_t* x, int64_t T, int64_t 
   return hip_status(e, fn);
 }
 
+mxfp8_status mxfp8_group_quantize_requant_noalloc(const uint16_t* x, int64_t T, int64_t K,
+                                                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                                  uint8_t* s_col, const int64_t* m_splits,
+                                                  int32_t G, float* dbias, void* stream) {
+  const char* fn = "mxfp8_group_quantize_requant_noalloc";
+  REQUIRE(T == 0 || (x && q_row && s_row && q_col && s_col), "%s: NULL data/scale pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  float* partial = nullptr;
+  if (dbias != nullptr) {
+    const size_t need = mxfp8_dbias_workspace_bytes(T, K);
+    REQUIRE(need <= mx::noalloc_scratch_bytes(),
+            "%s: dbias of a [%lld, %lld] operand needs %zu bytes of partial sums, more than the "
+            "%zu-byte static scratch (MXFP8_NOALLOC_SCRATCH_BYTES); use "
+            "mxfp8_group_quantize_requant with a workspace",
+            fn, (long long)T, (long long)K, need, mx::noalloc_scratch_bytes());
+    mxfp8_status st = check_device_splits(m_splits, G, fn);
+    if (st != MXFP8_OK) return st;
+    if (T > 0) {
+      const hipError_t e = mx::noalloc_scratch(&partial);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+  }
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0) e = mx::launch_quant_row_requant(x, T, K, q_row, s_row, q_col, s_col, partial, st);
+  if (e == hipSuccess && dbias != nullptr)
+    e = mx::launch_dbias_finalize(partial, m_splits, G, T, K, dbias, st);
+  return hip_status(e, fn);
+}
+
 mxfp8_status mxfp8_grouped_dbias(const uint8_t* q_row, const uint8_t* s_row, int64_t T,
                                  int64_t N, const int64_t* m_splits, int32_t G, float* dbias,
                                  void* workspace, size_t workspace_bytes, void* stream) {

@@ -39,6 +39,10 @@ hipError_t launch_swiglu_quant(const uint16_t* h, int64_t T, int64_t F, uint8_t*
 hipError_t launch_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                              uint16_t* dh, hipStream_t st);
 size_t convert_sweep_bytes(int32_t mode);   // 0 for an unknown mode
+// The file-scope device scratch of quantize.hip: its size, and its address on
+// the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(float** out);
 hipError_t launch_convert_sweep(int32_t mode, uint8_t* out, hipStream_t st);
 hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                const uint8_t* sb, void* c, bool out_bf16, int64_t T, int64_t N,

@@ -22,7 +22,9 @@
 //  * grouped bias gradient from row-wise data alone (PR #3244 Greptile
 //    Summary: ordinary dbias reduced directly without a wgrad stage).
 #include <algorithm>
+#include <mutex>
 
+#include "../../include/mxfp8moe.h"
 #include "mx_convert.h"
 #include "kernels.h"
 
@@ -1183,6 +1185,42 @@ hipError_t launch_swiglu_quant(const uint16_t* h, int64_t T, int64_t F, uint8_t*
   hipLaunchKernelGGL(swiglu_quant_kernel, grid, dim3(kColThreads), 0, st, h, T, F, q_row, s_row,
                      q_col, s_col);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (mxfp8_group_quantize_requant_
+// noalloc): the per-128-row fp32 dbias partials that the workspace of
+// mxfp8_group_quantize_requant holds, in a file-scope device array instead.
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name is
+// only a stand-in for the symbol): its device address is looked up once per
+// device, with that device current, and kept.
+constexpr size_t kScratchBytes = MXFP8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kScratchBytes; }
+
+hipError_t noalloc_scratch(float** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mx

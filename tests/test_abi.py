@@ -184,3 +184,18 @@ def test_binding_maps_errors(lib):
     with pytest.raises(RuntimeError):
         _native.check(3, "x")
     assert mx.ROWWISE == 1 and mx.COLWISE == 2
+
+
+def test_noalloc_quantize_requant_rejects(lib):
+    """The allocation-free fused quantize refuses, on the host, dbias partials
+    beyond its static scratch, and the usual shape errors."""
+    f = lib.mxfp8_group_quantize_requant_noalloc
+    assert mx.NOALLOC_SCRATCH_BYTES == 32 << 20
+    k = 14336
+    t_max = (mx.NOALLOC_SCRATCH_BYTES // (k * 4)) * 128     # 74880
+    st, msg = _status_msg(lib, f(FAKE, t_max + 128, k, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                 None))
+    assert st == 1 and "static scratch" in msg
+    assert f(FAKE, 100, 512, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1    # T % 128
+    assert f(FAKE, 128, 96, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1     # K % 512
+    assert f(None, 128, 512, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1    # NULL x

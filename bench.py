@@ -424,14 +424,20 @@ def _short_kernel(name):
     return n.replace("mx::", "")
 
 
-def _labels(names):
+def _labels(names, cycles=None):
     """Launch labels in dispatch order: the grouped GEMM's instantiations by
     layout (<false, *, false> alternates forward and dgrad, as every step
-    launches them in that order), every other kernel by its short name."""
-    out, mgrouped = [], {}
+    launches them in that order), every other kernel by its short name.
+    `cycles` maps a short kernel name to the names its successive launches
+    take in turn (a step that launches one kernel for several purposes)."""
+    out, mgrouped, seen = [], {}, {}
     for n in names:
         k = _short_kernel(n)
-        if k.startswith("grouped_gemm_kernel<"):
+        if cycles and k in cycles:
+            i = seen.get(k, 0)
+            seen[k] = i + 1
+            out.append(cycles[k][i % len(cycles[k])])
+        elif k.startswith("grouped_gemm_kernel<"):
             targs = [a.strip() for a in k[k.index("<") + 1:k.rindex(">")].split(",")]
             kg, bf, acc = (a == "true" for a in targs)
             dt = "_bf16" if bf else ""
@@ -539,14 +545,14 @@ Algorithmic bytes: codes and E8M0 scales read or written once, fp32 outputs and 
     return md
 
 
-def summarize_trace(trace_dir, title, commands, note=""):
+def summarize_trace(trace_dir, title, commands, note="", cycles=None):
     """Markdown table of a --kernel-trace run: per launch label (the GEMM by
     layout, in dispatch order), calls, mean / min / max duration and total."""
     import collections
     path = [os.path.join(trace_dir, x) for x in os.listdir(trace_dir)
             if x.endswith("kernel_trace.csv")][0]
     rows = _csv(path)
-    labels = _labels([r["Kernel_Name"] for r in rows])
+    labels = _labels([r["Kernel_Name"] for r in rows], cycles)
     d = collections.defaultdict(list)
     for r, lab in zip(rows, labels):
         d[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -567,7 +573,7 @@ Command (from the repository root, one MI355X):
 {cmd}
 ```
 
-From `{os.path.basename(path)}`, one row per launch label: the grouped GEMM's forward (`forward_NT`) and dgrad (`dgrad_NN`) are the two launches of `grouped_gemm_kernel<false, *, false>` in dispatch order, `wgrad_TN` is `<true, *, false>`, `wgrad_accumulate_TN` is `<true, false, true>`; a `_bf16` suffix marks bf16 outputs.  Written by `python bench.py --summarize trace ...`.
+From `{os.path.basename(path)}`, one row per launch label: the grouped GEMM's forward (`forward_NT`) and dgrad (`dgrad_NN`) are the two launches of `grouped_gemm_kernel<false, *, false>` in dispatch order, `wgrad_TN` is `<true, *, false>`, `wgrad_accumulate_TN` is `<true, false, true>`; a `_bf16` suffix marks bf16 outputs.""" + ("" if not cycles else "  Kernels launched for several purposes per step are named in launch order: " + "; ".join(f"`{k}` = {', '.join(v)}" for k, v in cycles.items()) + ".") + """  Written by `python bench.py --summarize trace ...`.
 
 """ + "\n".join(tab) + ("\n\n" + note if note else "") + "\n"
 
@@ -594,6 +600,8 @@ def summarize_main(argv):
                     help="the rocprofv3 command line(s) the CSVs came from (quoted in the file)")
     ap.add_argument("--dir", help="trace: the rocprofv3 output directory")
     ap.add_argument("--note", default="")
+    ap.add_argument("--cycle", action="append", default=[],
+                    help="trace: KERNEL=name1,name2,... names for successive launches of KERNEL")
     ap.add_argument("--workload", help="traffic: workload of the algorithmic bytes")
     ap.add_argument("--cal-fetch")
     ap.add_argument("--cal-write")
@@ -601,7 +609,8 @@ def summarize_main(argv):
     ap.add_argument("--write")
     a = ap.parse_args(argv)
     if a.kind == "trace":
-        md = summarize_trace(a.dir, a.title, a.command, a.note)
+        cycles = {c.split("=")[0]: c.split("=")[1].split(",") for c in a.cycle}
+        md = summarize_trace(a.dir, a.title, a.command, a.note, cycles or None)
     else:
         md = summarize_traffic(a.workload, a.cal_fetch, a.cal_write, a.fetch, a.write, a.title,
                                a.command)

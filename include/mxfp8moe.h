@@ -280,6 +280,36 @@ mxfp8_status mxfp8_grouped_gemm(int32_t layout, const uint8_t* a_data, const uin
                                 const int64_t* m_splits, int32_t G, void* stream);
 
 /*
+ * mxfp8_grouped_gemm_swiglu_quantize -- the forward (NT) grouped GEMM of the
+ * fused expert MLP's first linear, FC1, with its activation and the MXFP8
+ * quantize of the activation in the GEMM's epilogue ([P3545] Description:
+ * the fused grouped MLP runs FC1 -> activation -> FC2 as one op; its
+ * saved-state commit: the FC2 forward reads the row-wise tiles of the
+ * activation and the FC2 wgrad the column-wise ones).  The activation is
+ * SwiGLU (not defined on the pages): gate = columns [0, F) of h, up =
+ * columns [F, 2F).
+ *      h[r] = X[r] W1_g^T  (bf16, round to nearest even), r in expert g
+ *      a    = silu(gate) * up from the bf16 h, fp32 math, bf16 rounding
+ *      a quantized row-wise and/or column-wise
+ *  The outputs are byte-identical to mxfp8_grouped_gemm (NT, bf16 output)
+ *  followed by mxfp8_swiglu_quantize on its h; a itself is never written.
+ *   a_data/a_scale  X row-wise [T, K] + [T, K/32]
+ *   b_data/b_scale  W1 row-wise [G, 2F, K] + [G, 2F, K/32]
+ *   h               [T, 2F] bf16, written (the SwiGLU backward reads it)
+ *   usage           MXFP8_ROWWISE | MXFP8_COLWISE (at least one)
+ *   q_row [T, F] u8, s_row [T, F/32] u8     (required iff ROWWISE)
+ *   q_col [F, T] u8, s_col [F, T/32] u8     (required iff COLWISE)
+ * Errors: EINVAL for NULL required pointers, T % 128, F % 512, K % 512,
+ * G < 1 or G > 1024, host m_splits, usage == 0.
+ */
+mxfp8_status mxfp8_grouped_gemm_swiglu_quantize(const uint8_t* a_data, const uint8_t* a_scale,
+                                                const uint8_t* b_data, const uint8_t* b_scale,
+                                                uint16_t* h, int64_t T, int64_t F, int64_t K,
+                                                const int64_t* m_splits, int32_t G,
+                                                uint32_t usage, uint8_t* q_row, uint8_t* s_row,
+                                                uint8_t* q_col, uint8_t* s_col, void* stream);
+
+/*
  * mxfp8_grouped_gemm_wgrad_accumulate -- the TN (wgrad) product of
  * mxfp8_grouped_gemm added into an existing fp32 weight-gradient buffer
  * instead of overwriting it, the form a training step uses when the weight

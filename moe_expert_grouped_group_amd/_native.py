@@ -34,6 +34,9 @@ SIGNATURES = {
                                              c_i32, c_vp, c_vp, c_size, c_vp]),
     "mxfp8_group_quantize_requant_noalloc": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                                                      c_vp, c_i32, c_vp, c_vp]),
+    "mxfp8_grouped_gemm_swiglu_quantize": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                   c_i64, c_vp, c_i32, c_u32, c_vp, c_vp, c_vp,
+                                                   c_vp, c_vp]),
     "mxfp8_grouped_gemm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64,
                                    c_i64, c_vp, c_i32, c_vp]),
     "mxfp8_validate_splits": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp]),

@@ -357,6 +357,31 @@ def grouped_gemm(layout, a_data, a_scale, b_data, b_scale, m_splits, tokens, n, 
     return out
 
 
+def grouped_gemm_swiglu_quantize(a_data, a_scale, b_data, b_scale, m_splits, tokens, f, k,
+                                 usage=ROWWISE | COLWISE, h=None, out=None, stream=None):
+    """Forward of the fused MLP's FC1 with SwiGLU + quantize in the epilogue:
+    h [T, 2F] = X W1_g^T (bf16; a = X row-wise [T, k], b = W1 row-wise
+    [G, 2F, k]) and the MXFP8Tensor of a = silu(h[:, :F]) * h[:, F:] (the
+    bytes of grouped_gemm + swiglu_quantize).  Returns (h, MXFP8Tensor)."""
+    lib = _lib()
+    ms = _splits(m_splits)
+    g = ms.numel()
+    t = tokens
+    a2 = _as_shape(a_data, (t, k), "a_data")
+    as2 = _as_shape(a_scale, (t, k // 32), "a_scale")
+    b2 = _as_shape(b_data, (g * 2 * f, k), "b_data")
+    bs2 = _as_shape(b_scale, (g * 2 * f, k // 32), "b_scale")
+    if h is None:
+        h = _empty((t, 2 * f), torch.bfloat16, a2)
+    _need(h, torch.bfloat16, (t, 2 * f), "h")
+    out = _mx_outputs(out, usage, t, f, a2)
+    st = lib.mxfp8_grouped_gemm_swiglu_quantize(
+        _ptr(a2), _ptr(as2), _ptr(b2), _ptr(bs2), _ptr(h), t, f, k, _ptr(ms), g, usage,
+        *_mx_ptrs(out, usage), _stream(stream))
+    _native.check(st, "mxfp8_grouped_gemm_swiglu_quantize")
+    return h, out
+
+
 def grouped_gemm_wgrad_accumulate(a_data, a_scale, b_data, b_scale, m_splits, tokens, n, k,
                                   main_grad, stream=None, workspace=None):
     """wgrad added into an fp32 main_grad [G, n, k] in place:

@@ -266,6 +266,38 @@ static mxfp8_status grouped_gemm_impl(const char* fn, int32_t layout, const uint
   return hip_status(e, fn);
 }
 
+mxfp8_status mxfp8_grouped_gemm_swiglu_quantize(const uint8_t* a_data, const uint8_t* a_scale,
+                                                const uint8_t* b_data, const uint8_t* b_scale,
+                                                uint16_t* h, int64_t T, int64_t F, int64_t K,
+                                                const int64_t* m_splits, int32_t G,
+                                                uint32_t usage, uint8_t* q_row, uint8_t* s_row,
+                                                uint8_t* q_col, uint8_t* s_col, void* stream) {
+  const char* fn = "mxfp8_grouped_gemm_swiglu_quantize";
+  REQUIRE(usage != 0 && (usage & ~(MXFP8_ROWWISE | MXFP8_COLWISE)) == 0,
+          "%s: usage must be a non-empty combination of MXFP8_ROWWISE and MXFP8_COLWISE", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(F > 0 && F % 512 == 0, "%s: F = %lld must be a positive multiple of 512", fn,
+          (long long)F);
+  REQUIRE(K > 0 && K % 512 == 0, "%s: K = %lld must be a positive multiple of 512", fn,
+          (long long)K);
+  REQUIRE(G <= 1024, "%s: G = %d exceeds the supported 1024 experts", fn, (int)G);
+  if (T > 0) {
+    REQUIRE(a_data && a_scale && b_data && b_scale && h, "%s: NULL operand pointer", fn);
+    const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
+    REQUIRE(!row || (q_row && s_row), "%s: ROWWISE requested but q_row/s_row is NULL", fn);
+    REQUIRE(!col || (q_col && s_col), "%s: COLWISE requested but q_col/s_col is NULL", fn);
+  }
+  mxfp8_status s = check_device_splits(m_splits, G, fn);
+  if (s != MXFP8_OK) return s;
+  if (T == 0) return ok();   // no rows: every output is empty
+  const bool row = usage & MXFP8_ROWWISE, col = usage & MXFP8_COLWISE;
+  return hip_status(mx::launch_grouped_gemm_swiglu(a_data, a_scale, b_data, b_scale, h, T, F, K,
+                                                   m_splits, G, row ? q_row : nullptr,
+                                                   row ? s_row : nullptr, col ? q_col : nullptr,
+                                                   col ? s_col : nullptr, as_stream(stream)),
+                    fn);
+}
+
 static mxfp8_status wgrad_accumulate_impl(const char* fn, const uint8_t* a_data,
                                           const uint8_t* a_scale, const uint8_t* b_data,
                                           const uint8_t* b_scale, float* main_grad, int64_t T,

@@ -44,6 +44,7 @@
 #include <algorithm>
 
 #include "mx_device.h"
+#include "mx_tile_quant.h"
 #include "kernels.h"
 
 namespace mx {
@@ -80,6 +81,16 @@ struct GemmArgs {
   int32_t ntiles;                      // K-grouped: G * band * ntiles_n tiles
   int32_t split_tail;                  // M-grouped, fp32 out: split the last round's tiles
   int32_t* queue;                      // K-grouped: tile counter (dynamic order), or NULL
+  // SwiGLU epilogue (forward with bf16 output only): C = h [T, 2F] holds gate
+  // columns [0, F) and up columns [F, 2F); each tile pairs gate columns
+  // [128 nt, 128 nt + 128) with the up columns F later, and the epilogue also
+  // writes a = silu(gate) * up quantized row-wise ([T, F] + [T, F/32]) and/or
+  // column-wise ([F, T] + [F, T/32]).
+  int64_t f;
+  uint8_t* q_row;
+  uint8_t* s_row;
+  uint8_t* q_col;
+  uint8_t* s_col;
 };
 
 // LDS layout of one stage: A tile [BM][BK], B tile [BN][BK]; 16-byte chunk c
@@ -284,9 +295,11 @@ struct TileDesc {
   int32_t rows_avail;  // copied rows inside the operand (256, or T when T < 256)
   int32_t nblk;        // scale blocks of the tile's contraction (nk * 2)
   int32_t split;       // one contraction half of a split tile: add into C atomically
+  int64_t m0c;         // M-grouped: first copied row (token) of the tile
+  int32_t nt;          // M-grouped: column tile index
 };
 
-template <bool KGROUPED>
+template <bool KGROUPED, bool SWIGLU = false>
 __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTable* t, int tile,
                                              int64_t esz, int dynamic = 0) {
   TileDesc d;
@@ -300,7 +313,9 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     }
     const int g = lo;
     const int64_t m0 = t->roff[g] + (int64_t)(mt - t->tpre[g]) * BM;
-    const int64_t n0 = (int64_t)nt * BN;
+    // SwiGLU: the tile's first B row (and C column) is gate column 128 nt;
+    // its up half lies F rows (columns) further on (setup, epilogue)
+    const int64_t n0 = (int64_t)nt * (SWIGLU ? BN / 2 : BN);
     const int64_t end = min(t->roff[g + 1], p.rows);   // never past the token count
     const int64_t valid = max(min((int64_t)BM, end - m0), (int64_t)0);
     // The 256 copied rows start at m0c: moved back from the tile's first row
@@ -317,6 +332,8 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.nk = valid > 0 ? (int32_t)(p.kc / KSTEP) : 0;
     d.nblk = (int32_t)(p.kc / 32);
     d.c = reinterpret_cast<char*>(p.c) + (m0c * p.ldc + n0) * esz;
+    d.m0c = m0c;
+    d.nt = nt;
   } else {
     // The list of tiles (experts in decreasing order of tokens) is consumed
     // from both ends at once: of the two workgroups of a pair (tiles 2q and
@@ -431,11 +448,11 @@ __device__ __forceinline__ UnitPlan plan_units(const GemmArgs& p, const ExpertTa
   return u;
 }
 
-template <bool KGROUPED>
+template <bool KGROUPED, bool SWIGLU = false>
 __device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const ExpertTable* t,
                                                   const UnitPlan& up, int unit, int64_t esz) {
-  if (KGROUPED || unit < up.first_split) {
-    TileDesc d = describe<KGROUPED>(p, t, unit, esz, up.dynamic);
+  if (KGROUPED || SWIGLU || unit < up.first_split) {
+    TileDesc d = describe<KGROUPED, SWIGLU>(p, t, unit, esz, up.dynamic);
     d.split = 0;
     return d;
   }
@@ -456,8 +473,11 @@ __device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const Exper
 }
 
 // ACCUM (wgrad with fp32 output only): C += the product instead of C = it.
-template <bool KGROUPED, bool OUT_BF16, bool ACCUM = false>
+// SWIGLU (forward with bf16 output only): the SwiGLU + quantize epilogue
+// (GemmArgs.f and the q/s outputs).
+template <bool KGROUPED, bool OUT_BF16, bool ACCUM = false, bool SWIGLU = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
+  static_assert(!SWIGLU || (!KGROUPED && OUT_BF16 && !ACCUM), "SwiGLU epilogue: forward, bf16");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
   __shared__ int32_t next_lds;          // dynamic order: the next tile, from thread 0
@@ -497,8 +517,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     const int64_t wrow = (int64_t)((wave * 64) % d.rows_avail);
     a_base = uniform_ptr(d.a + wrow * p.lda);
     sa_base = uniform_ptr(d.sa + wrow * p.ldsa);
-    b_base = uniform_ptr(d.b + (int64_t)wave * 64 * p.ldb);
-    sb_base = uniform_ptr(d.sb + (int64_t)wave * 64 * p.ldsb);
+    // SwiGLU: waves 2 and 3 copy the up rows, F rows after the gate rows
+    const int64_t brow = (int64_t)wave * 64 + (SWIGLU && wave >= 2 ? p.f - BN / 2 : 0);
+    b_base = uniform_ptr(d.b + brow * p.ldb);
+    sb_base = uniform_ptr(d.sb + brow * p.ldsb);
     s_nblk = d.nblk;
   };
   // LDS byte addresses of the stages and of the scale buffers (the low half
@@ -618,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   if (ACCUM && up.dynamic) up.dynamic = 2;   // blocked order (describe)
   int tile = blockIdx.x;   // unit index (a tile, or half of one: describe_unit)
   if (tile >= up.nunits) return;
-  TileDesc cur = describe_unit<KGROUPED>(p, &table, up, tile, esz);
+  TileDesc cur = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
   setup(cur);
   tile_prologue(cur.nk);
   // A tile's first wait leaves 63 vector-memory operations outstanding.  It
@@ -795,7 +817,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     }
     TileDesc nxt;
     nxt.nk = 0;
-    if (next < up.nunits) {
+    // (SwiGLU: the epilogue uses the LDS, so the next tile's copies wait
+    // until after it)
+    if (!SWIGLU && next < up.nunits) {
       nxt = describe_unit<KGROUPED>(p, &table, up, next, esz);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
@@ -807,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // expert table (LDS) rather than kept from the tile start: held across
     // the K loop they are spilled, and the reload's wait on the vector memory
     // counter would also wait for the next tile's copies issued above.
-    const TileDesc ed = describe_unit<KGROUPED>(p, &table, up, tile, esz);
+    const TileDesc ed = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
 
     // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
     // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32.
@@ -825,7 +849,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     if (!KGROUPED) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
-      const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (int64_t)(wn * WT + fr) * esz);
+      // SwiGLU: the up wave's columns lie F after the gate wave's
+      const int64_t wcol = SWIGLU ? wn * p.f : wn * WT;
+      const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (wcol + fr) * esz);
       const int lo = ed.row_lo, hi = ed.row_hi;
       const bool part = lo > 0 || hi < BM;
       // a contraction half of a split tile adds into C (branch outside the
@@ -863,6 +889,83 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
                     acc[i][j][r], (__attribute__((address_space(1))) float*)(rbase + j * 32 * 4));
             }
           }
+        }
+      }
+      if (SWIGLU) {
+        // SwiGLU + quantize of the tile: a = silu(gate) * up for the 256 x 128
+        // gate/up pairs (gate in waves wn = 0, up in waves wn = 1, same rows
+        // and columns), formed from the bf16-rounded h exactly as
+        // swiglu_pair does, staged in LDS as two 128 x 128 bf16 tiles (rows
+        // 128 s.. of the copied rows) in the layout of the streaming quantize
+        // kernels, then quantized by their row- and column-wise passes: the
+        // bytes of mxfp8_swiglu_quantize on the h written above.
+        // MFMA layout: register r of fragment (i, j) in lane l is row
+        // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 j + l % 32 of the
+        // wave's 128 x 128 block; (row >> 4) = 2 i + (r >= 8), so the lane's
+        // part of the LDS offset is 4 (l / 32) rows and 2 (l % 32) bytes.
+        // the accumulators as the compiler must re-read them: otherwise it
+        // keeps the bf16 values of the h stores above live until here
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last stage
+        __syncthreads();                      // every wave's: the stage slots are free
+        uint8_t* sub = smem + wm_u * kLdsBytesBf16;
+        uint32_t ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int lane_lds = (int)(4 * (ln >> 5) * 256 + 2 * (ln & 31));
+        if (wn == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r / 4) + (r % 4);
+                *reinterpret_cast<uint16_t*>(sub + lds_off_bf16(row, 64 * j) + lane_lds) =
+                    (uint16_t)f32_to_bf16(acc[i][j][r]);
+              }
+        }
+        __syncthreads();
+        if (wn == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r / 4) + (r % 4);
+                uint16_t* e = reinterpret_cast<uint16_t*>(sub + lds_off_bf16(row, 64 * j) + lane_lds);
+                const float g = bf16_to_f32(f32_to_bf16(acc[i][j][r]));
+                *e = (uint16_t)f32_to_bf16(silu_f(g) * bf16_to_f32(*e));
+              }
+        }
+        __syncthreads();
+        // the thread index from the hardware here (volatile: not hoisted),
+        // so that the passes' per-thread offsets are formed here and not
+        // kept in registers through the K loop
+        uint32_t tq;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(tq));
+        tq += 64 * (uint32_t)wave;
+        // sub-tiles wholly inside the tile's rows (row_lo and row_hi are
+        // multiples of 128: expert runs are)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (128 * s2 < lo || 128 * s2 + 128 > hi) continue;
+          const uint8_t* st_lds = smem + s2 * kLdsBytesBf16;
+          const int64_t t0 = ed.m0c + 128 * s2, k0 = (int64_t)ed.nt * 128;
+          if (p.q_row != nullptr)
+            rowwise_pass_bf16(st_lds, p.f, k0, t0, p.q_row, p.s_row, (int)tq);
+          if (p.q_col != nullptr)
+            colwise_pass_bf16<false>(st_lds, p.rows, p.f, k0, t0, p.q_col, p.s_col, (int)tq);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __syncthreads();                      // the LDS is free for the next tile's copies
+        if (next < up.nunits) {
+          nxt = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+          setup(nxt);
+          tile_prologue(nxt.nk);
         }
       }
     }
@@ -947,7 +1050,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // the store loops above issue one operation per register (M-grouped: 256
     // per wave, every row inside the tile) or per 4 registers (K-grouped: 64
     // stores, plus 64 loads when accumulating)
-    if (!(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
+    // (SwiGLU: the next tile's copies were issued last; wait for them)
+    if (SWIGLU || !(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     tile = next;
     cur = nxt;
@@ -988,9 +1092,10 @@ __global__ void queue_init_kernel(int32_t* queue, int32_t grid) {
   }
 }
 
-template <bool KG, bool BF, bool ACC = false>
+template <bool KG, bool BF, bool ACC = false, bool SW = false>
 static hipError_t launch_one(const GemmArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<KG, BF, ACC>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<KG, BF, ACC, SW>), dim3(grid), dim3(kThreads), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -1062,6 +1167,39 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
   if (kgrouped)
     return out_bf16 ? launch_one<true, true>(p, grid, st) : launch_one<true, false>(p, grid, st);
   return out_bf16 ? launch_one<false, true>(p, grid, st) : launch_one<false, false>(p, grid, st);
+}
+
+// Forward (NT) with bf16 h [T, 2F] and the SwiGLU + quantize epilogue.
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                                      const uint8_t* sb, uint16_t* h, int64_t T, int64_t F,
+                                      int64_t K, const int64_t* m_splits, int32_t G,
+                                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                      uint8_t* s_col, hipStream_t st) {
+  GemmArgs p{};
+  p.a = a;
+  p.sa = sa;
+  p.b = b;
+  p.sb = sb;
+  p.c = h;
+  p.m_splits = m_splits;
+  p.G = G;
+  const int64_t N = 2 * F;
+  p.lda = K; p.ldsa = K / 32;
+  p.ldb = K; p.ldsb = K / 32;
+  p.b_gstride = N * K; p.sb_gstride = N * K / 32;
+  p.ldc = N; p.rows = T; p.cols = N; p.kc = K;
+  p.ntiles_n = (int32_t)(N / BN);
+  p.f = F;
+  p.q_row = q_row;
+  p.s_row = s_row;
+  p.q_col = q_col;
+  p.s_col = s_col;
+  const int64_t upper = (T / BM + G) * p.ntiles_n;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(upper, cus));
+  return launch_one<false, true, false, true>(p, grid, st);
 }
 
 }  // namespace mx

@@ -48,5 +48,12 @@ hipError_t launch_grouped_gemm(int layout, const uint8_t* a, const uint8_t* sa, 
                                const uint8_t* sb, void* c, bool out_bf16, int64_t T, int64_t N,
                                int64_t K, const int64_t* m_splits, int32_t G, bool accumulate,
                                hipStream_t st, int32_t* queue = nullptr);
+// Forward NT with bf16 h [T, 2F] (gate | up), fused with the SwiGLU of h and
+// the row- and/or column-wise quantize of a = silu(gate) * up [T, F].
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                                      const uint8_t* sb, uint16_t* h, int64_t T, int64_t F,
+                                      int64_t K, const int64_t* m_splits, int32_t G,
+                                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                      uint8_t* s_col, hipStream_t st);
 
 }  // namespace mx

@@ -199,3 +199,19 @@ def test_noalloc_quantize_requant_rejects(lib):
     assert f(FAKE, 100, 512, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1    # T % 128
     assert f(FAKE, 128, 96, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1     # K % 512
     assert f(None, 128, 512, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == 1    # NULL x
+
+
+def test_swiglu_gemm_rejects(lib):
+    """FC1 with the SwiGLU + quantize epilogue: shape and usage errors on the
+    host."""
+    f = lib.mxfp8_grouped_gemm_swiglu_quantize
+    ops = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    outs = (FAKE, FAKE, FAKE, FAKE)
+    assert f(*ops, 128, 512, 512, FAKE, 1, 0, *outs, None) == 1            # no usage
+    assert f(*ops, 128, 512, 512, FAKE, 1, 4, *outs, None) == 1            # unknown usage bit
+    assert f(*ops, 100, 512, 512, FAKE, 1, 3, *outs, None) == 1            # T % 128
+    assert f(*ops, 128, 256, 512, FAKE, 1, 3, *outs, None) == 1            # F % 512
+    assert f(*ops, 128, 512, 500, FAKE, 1, 3, *outs, None) == 1            # K % 512
+    assert f(*ops, 128, 512, 512, FAKE, 1025, 3, *outs, None) == 1         # G > 1024
+    st, msg = _status_msg(lib, f(*ops, 128, 512, 512, FAKE, 1, 2, FAKE, FAKE, None, None, None))
+    assert st == 1 and "COLWISE" in msg                                    # col without buffers

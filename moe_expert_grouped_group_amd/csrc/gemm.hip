@@ -202,6 +202,15 @@ __device__ __forceinline__ void quad_transpose(float& v0, float& v1, float& v2, 
   v3 = hi2 ? v3 : y;
 }
 
+// Two fp32 values -> a bf16 pair (round to nearest even; the first value in
+// the low half): one V_CVT_PK_BF16_F32, the same bits as f32_to_bf16 for
+// finite values.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
 // Expert table kept in LDS for the whole launch: exclusive prefix of tiles
 // (forward/dgrad: ceil(M_g / BM) row tiles per expert) and of token rows, and
 // (wgrad) the experts in decreasing order of tokens.
@@ -478,6 +487,8 @@ __device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const Exper
 template <bool KGROUPED, bool OUT_BF16, bool ACCUM = false, bool SWIGLU = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(!SWIGLU || (!KGROUPED && OUT_BF16 && !ACCUM), "SwiGLU epilogue: forward, bf16");
+  static_assert(4 * kLdsBytesBf16 <= kSlots * kStageBytes + 2 * kScaleBuf,
+                "SwiGLU epilogue: four staged 128 x 128 bf16 tiles fit the stage buffers");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
   __shared__ int32_t next_lds;          // dynamic order: the next tile, from thread 0
@@ -894,71 +905,64 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       if (SWIGLU) {
         // SwiGLU + quantize of the tile: a = silu(gate) * up for the 256 x 128
         // gate/up pairs (gate in waves wn = 0, up in waves wn = 1, same rows
-        // and columns), formed from the bf16-rounded h exactly as
-        // swiglu_pair does, staged in LDS as two 128 x 128 bf16 tiles (rows
-        // 128 s.. of the copied rows) in the layout of the streaming quantize
-        // kernels, then quantized by their row- and column-wise passes: the
-        // bytes of mxfp8_swiglu_quantize on the h written above.
+        // and columns).  Every wave stages its bf16-rounded h block in LDS as
+        // a 128 x 128 tile in the layout of the streaming quantize kernels
+        // (gate tiles 0, 1 for rows 0..127 and 128..255 of the copied rows, up
+        // tiles 2, 3); then all 256 threads form a as swiglu_pair does and
+        // quantize it row-wise from registers, writing a over the gate tile,
+        // and run the column-wise pass on it: the bytes of
+        // mxfp8_swiglu_quantize on the h written above.
         // MFMA layout: register r of fragment (i, j) in lane l is row
         // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 j + l % 32 of the
         // wave's 128 x 128 block; (row >> 4) = 2 i + (r >= 8), so the lane's
         // part of the LDS offset is 4 (l / 32) rows and 2 (l % 32) bytes.
-        // the accumulators as the compiler must re-read them: otherwise it
-        // keeps the bf16 values of the h stores above live until here
+        // The accumulators as the compiler must re-read them: otherwise it
+        // keeps the bf16 values of the h stores above live until here.
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last stage
         __syncthreads();                      // every wave's: the stage slots are free
-        uint8_t* sub = smem + wm_u * kLdsBytesBf16;
+        uint8_t* sub = smem + (2 * wn + wm_u) * kLdsBytesBf16;
         uint32_t ln;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
         const int lane_lds = (int)(4 * (ln >> 5) * 256 + 2 * (ln & 31));
-        if (wn == 1) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r / 4) + (r % 4);
-                *reinterpret_cast<uint16_t*>(sub + lds_off_bf16(row, 64 * j) + lane_lds) =
-                    (uint16_t)f32_to_bf16(acc[i][j][r]);
-              }
-        }
-        __syncthreads();
-        if (wn == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r / 4) + (r % 4);
-                uint16_t* e = reinterpret_cast<uint16_t*>(sub + lds_off_bf16(row, 64 * j) + lane_lds);
-                const float g = bf16_to_f32(f32_to_bf16(acc[i][j][r]));
-                *e = (uint16_t)f32_to_bf16(silu_f(g) * bf16_to_f32(*e));
-              }
-        }
+            for (int r = 0; r < 16; r += 2) {
+              // registers r, r + 1: rows R, R + 1 of one column
+              const int row = 32 * i + 8 * (r / 4) + (r % 4);
+              const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+              uint8_t* e = sub + lds_off_bf16(row, 64 * j) + lane_lds;
+              *reinterpret_cast<uint16_t*>(e) = (uint16_t)pk;
+              *reinterpret_cast<uint16_t*>(e + 256) = (uint16_t)(pk >> 16);
+            }
         __syncthreads();
         // the thread index from the hardware here (volatile: not hoisted),
         // so that the passes' per-thread offsets are formed here and not
         // kept in registers through the K loop
-        uint32_t tq;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(tq));
-        tq += 64 * (uint32_t)wave;
+        const int tq = (int)(ln + 64 * (uint32_t)wave);
+        const int64_t k0 = (int64_t)ed.nt * 128;
         // sub-tiles wholly inside the tile's rows (row_lo and row_hi are
         // multiples of 128: expert runs are)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (128 * s2 < lo || 128 * s2 + 128 > hi) continue;
-          const uint8_t* st_lds = smem + s2 * kLdsBytesBf16;
-          const int64_t t0 = ed.m0c + 128 * s2, k0 = (int64_t)ed.nt * 128;
-          if (p.q_row != nullptr)
-            rowwise_pass_bf16(st_lds, p.f, k0, t0, p.q_row, p.s_row, (int)tq);
-          if (p.q_col != nullptr)
-            colwise_pass_bf16<false>(st_lds, p.rows, p.f, k0, t0, p.q_col, p.s_col, (int)tq);
+          swiglu_rowwise_pass(smem + s2 * kLdsBytesBf16, smem + (2 + s2) * kLdsBytesBf16, p.f,
+                              k0, ed.m0c + 128 * s2, p.q_row, p.s_row, p.q_col != nullptr, tq);
+        }
+        if (p.q_col != nullptr) {
+          __syncthreads();
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            if (128 * s2 < lo || 128 * s2 + 128 > hi) continue;
+            colwise_pass_bf16<false>(smem + s2 * kLdsBytesBf16, p.rows, p.f, k0,
+                                     ed.m0c + 128 * s2, p.q_col, p.s_col, tq);
+          }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __syncthreads();                      // the LDS is free for the next tile's copies

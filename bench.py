@@ -368,6 +368,11 @@ def bench_fused_mlp(steps, warmup):
                                    ms, t, n2, k, bf, dw1, workspace=gws)),
     ]
     ms_step, per = _run_steps(launches, steps, warmup)
+    # FC1 with the SwiGLU + quantize in its epilogue (same h and bytes as
+    # fc1_fprop + swiglu_quant), timed outside the step
+    fused_ms = _time_outside(lambda: mx.grouped_gemm_swiglu_quantize(
+        xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale, ms, t, f, k, h=h, out=ao),
+        steps)
     flops = 3 * 2.0 * t * k * n2 + 3 * 2.0 * t * f * k
     gemm_ms = sum(v for nm, v in per.items() if nm.startswith("fc"))
     return {
@@ -378,6 +383,10 @@ def bench_fused_mlp(steps, warmup):
         "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
         "gemm_frac_of_peak": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
         "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
+        "fc1_swiglu_quantize_fused_ms": round(fused_ms, 4),
+        "note": "the step launches FC1 and swiglu_quant separately; "
+                "fc1_swiglu_quantize_fused_ms is the one-launch form "
+                "(mxfp8_grouped_gemm_swiglu_quantize), timed outside the step",
     }
 
 
@@ -438,10 +447,12 @@ def _labels(names, cycles=None):
             seen[k] = i + 1
             out.append(cycles[k][i % len(cycles[k])])
         elif k.startswith("grouped_gemm_kernel<"):
-            targs = [a.strip() for a in k[k.index("<") + 1:k.rindex(">")].split(",")]
-            kg, bf, acc = (a == "true" for a in targs)
+            targs = [a.strip() == "true" for a in k[k.index("<") + 1:k.rindex(">")].split(",")]
+            kg, bf, acc = targs[:3]
             dt = "_bf16" if bf else ""
-            if acc:
+            if len(targs) > 3 and targs[3]:
+                out.append("forward_NT_swiglu_quantize")
+            elif acc:
                 out.append("wgrad_accumulate_TN")
             elif kg:
                 out.append("wgrad_TN" + dt)
@@ -464,6 +475,16 @@ def algorithmic_bytes(workload):
         t, k = 131072, 7168
         return {"quant_rowcol_kernel": t * k * (2 + 2 * sc)}
     g, t = len(wl.splits_for(workload)), int(wl.splits_for(workload).sum())
+    if workload == "nemotron_proxy_mlp":
+        k, n2, f = 3072, 2048, 1024
+        return {
+            "fc1_fprop": t * k * sc + g * n2 * k * sc + t * n2 * 2,
+            "fc2_fprop": t * f * sc + g * k * f * sc + t * k * 2,
+            "fc2_dgrad": t * k * sc + g * k * f * sc + t * f * 2,
+            "fc1_dgrad": t * n2 * sc + g * n2 * k * sc + t * k * 2,
+            "fc2_wgrad": t * k * sc + t * f * sc + g * k * f * 2,
+            "fc1_wgrad": t * n2 * sc + t * k * sc + g * n2 * k * 2,
+        }
     k, n = {"moe8_h4096_f14336": (4096, 14336)}[workload]
     return {
         "forward_NT": t * k * sc + g * n * k * sc + t * n * 4,
@@ -477,11 +498,11 @@ def algorithmic_bytes(workload):
     }
 
 
-def _counter_means(path):
+def _counter_means(path, cycles=None):
     """Mean counter value and duration (us) per launch label of a --pmc CSV."""
     import collections
     rows = _csv(path)
-    labels = _labels([r["Kernel_Name"] for r in rows])
+    labels = _labels([r["Kernel_Name"] for r in rows], cycles)
     vals, durs = collections.defaultdict(list), collections.defaultdict(list)
     for r, lab in zip(rows, labels):
         vals[lab].append(float(r["Counter_Value"]))
@@ -491,7 +512,7 @@ def _counter_means(path):
             {k: sum(v) / len(v) for k, v in durs.items()})
 
 
-def summarize_traffic(workload, cal_fetch, cal_write, fetch, write, title, commands):
+def summarize_traffic(workload, cal_fetch, cal_write, fetch, write, title, commands, cycles=None):
     """Markdown + JSON of HBM bytes per launch from FETCH_SIZE and WRITE_SIZE
     runs, scaled by the same counters on the 1 GiB copy of --calibrate-copy."""
     cf, _, _ = _counter_means(os.path.join(cal_fetch, "p_counter_collection.csv"))
@@ -499,8 +520,8 @@ def summarize_traffic(workload, cal_fetch, cal_write, fetch, write, title, comma
     copy = [k for k in cf if "copyBuffer" in k][0]
     ff = round(COPY_BYTES / 1024 / cf[copy], 4)
     fw = round(COPY_BYTES / 1024 / cw[copy], 4)
-    f, nf, df = _counter_means(os.path.join(fetch, "p_counter_collection.csv"))
-    w, _, _ = _counter_means(os.path.join(write, "p_counter_collection.csv"))
+    f, nf, df = _counter_means(os.path.join(fetch, "p_counter_collection.csv"), cycles)
+    w, _, _ = _counter_means(os.path.join(write, "p_counter_collection.csv"), cycles)
     alg = algorithmic_bytes(workload)
     per, tab = {}, []
     for lab in sorted(f, key=lambda x: (x not in alg, x)):
@@ -578,6 +599,49 @@ From `{os.path.basename(path)}`, one row per launch label: the grouped GEMM's fo
 """ + "\n".join(tab) + ("\n\n" + note if note else "") + "\n"
 
 
+def summarize_mfma(pmc_dir, title, commands, cycles=None):
+    """Markdown of a --pmc run with GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES
+    and SQ_INSTS_VALU_MFMA_MOPS_F8: per launch label the duration, the mean
+    shader clock (active cycles of one XCD over the duration), the matrix
+    cores' busy fraction of the active SIMD cycles, and the F8 MFMA work."""
+    import collections
+    import statistics as st
+    rows = _csv(os.path.join(pmc_dir, "p_counter_collection.csv"))
+    by = collections.OrderedDict()
+    for r in rows:
+        d = by.setdefault(int(r["Dispatch_Id"]), {
+            "name": r["Kernel_Name"],
+            "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    labels = _labels([d["name"] for d in by.values()], cycles)
+    agg = collections.defaultdict(list)
+    for d, lab in zip(by.values(), labels):
+        gui = d["GRBM_GUI_ACTIVE"] / 8          # summed over the 8 XCDs
+        agg[lab].append((d["dur"] / 1e3, gui / d["dur"],
+                         d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024),
+                         d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / 1e12))
+    tab = ["| launch | launches | duration us (mean) | clock GHz (active cycles / duration) | "
+           "MFMA busy (of active SIMD cycles) | F8 MFMA work, TFLOP |", "|---|---|---|---|---|---|"]
+    for lab, v in agg.items():
+        m = lambda i: st.mean(x[i] for x in v)  # noqa: E731
+        tab.append(f"| {lab} | {len(v)} | {m(0):.0f} | {m(1):.2f} (range "
+                   f"{min(x[1] for x in v):.2f}-{max(x[1] for x in v):.2f}) | {100 * m(2):.1f} % | "
+                   f"{m(3):.3f} |")
+    cmd = "\n".join(commands)
+    return f"""# {title}
+
+Command (from the repository root, one MI355X; one run, every counter in it within the hardware's per-block limits):
+
+```
+{cmd}
+```
+
+""" + "\n".join(tab) + """
+
+Per launch: GRBM_GUI_ACTIVE is summed over the 8 XCDs, so divided by 8 and by the launch's duration (its timestamps in the same CSV) it is the mean shader clock; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs); F8 MFMA work = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 (the counter's unit is 512 multiply-adds; the scaled FP8 MFMA counts as F8).  Durations are longer than bench.py's event times (counter collection serialises the launches).  Written by `python bench.py --summarize mfma ...`.
+"""
+
+
 def quantize_source_hash():
     h = hashlib.sha256()
     for rel in ["moe_expert_grouped_group_amd/csrc/quantize.hip",
@@ -593,12 +657,12 @@ def quantize_source_hash():
 
 def summarize_main(argv):
     ap = argparse.ArgumentParser(prog="bench.py --summarize")
-    ap.add_argument("kind", choices=["trace", "traffic"])
+    ap.add_argument("kind", choices=["trace", "traffic", "mfma"])
     ap.add_argument("--out", required=True, help="markdown file to write")
     ap.add_argument("--title", required=True)
     ap.add_argument("--command", action="append", default=[],
                     help="the rocprofv3 command line(s) the CSVs came from (quoted in the file)")
-    ap.add_argument("--dir", help="trace: the rocprofv3 output directory")
+    ap.add_argument("--dir", help="trace, mfma: the rocprofv3 output directory")
     ap.add_argument("--note", default="")
     ap.add_argument("--cycle", action="append", default=[],
                     help="trace: KERNEL=name1,name2,... names for successive launches of KERNEL")
@@ -608,12 +672,14 @@ def summarize_main(argv):
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     a = ap.parse_args(argv)
+    cycles = {c.split("=")[0]: c.split("=")[1].split(",") for c in a.cycle}
     if a.kind == "trace":
-        cycles = {c.split("=")[0]: c.split("=")[1].split(",") for c in a.cycle}
         md = summarize_trace(a.dir, a.title, a.command, a.note, cycles or None)
+    elif a.kind == "mfma":
+        md = summarize_mfma(a.dir, a.title, a.command, cycles or None)
     else:
         md = summarize_traffic(a.workload, a.cal_fetch, a.cal_write, a.fetch, a.write, a.title,
-                               a.command)
+                               a.command, cycles or None)
     with open(a.out, "w") as f:
         f.write(md)
     print(md)

@@ -41,6 +41,7 @@
 //    while the current step's MFMAs run, one read per MFMA.  Odd steps open
 //    with the only wait and barrier, then interleave the copies of the stage
 //    two ahead with their MFMAs.
+#include <type_traits>
 #include <algorithm>
 
 #include "mx_device.h"
@@ -853,16 +854,27 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // again here, and kept out of L2 it leaves room for the operand panels
     // the other workgroups on the XCD are still reading (2 % faster forward
     // and wgrad; the accumulating wgrad's old values are read the same way).
-    // Forward and dgrad (long contractions): one store instruction per
-    // register writes 32 consecutive columns of two rows, whole 128-byte
-    // lines for fp32 output.  (The 16-byte form below measured 2 % slower
-    // here: its transposes cost more than the store instructions it saves.)
-    if (!KGROUPED) {
+    // Forward, dgrad and the plain wgrad: one store instruction per register
+    // writes 32 consecutive columns of two rows, whole 128-byte lines for
+    // fp32 output (K-grouped, C is [G][N][K] and the tile's rows are N
+    // rows).  With the scalar-base address form this beats the 16-byte
+    // transposed form of the accumulating wgrad below, whose DPP transposes
+    // cost more than the store instructions they save (wgrad 5 % faster,
+    // the fused MLP's bf16 FC1 wgrad 17 %).
+    // (SwiGLU: the h block is stored like any bf16 output first.)
+    if (!KGROUPED || !ACCUM) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
       // SwiGLU: the up wave's columns lie F after the gate wave's
       const int64_t wcol = SWIGLU ? wn * p.f : wn * WT;
-      const uint32_t lane_off = (uint32_t)(4 * fg * ldc_b + (wcol + fr) * esz);
+      // the lane's part of the store address, formed here from the hardware
+      // lane id (volatile: not hoisted and kept through the K loop) as a
+      // 32-bit offset to a scalar row base: the scalar-base store form, with
+      // no 64-bit vector address arithmetic per row (forward 3 % faster)
+      uint32_t ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const uint32_t lane_off =
+          (ln >> 5) * 4u * (uint32_t)ldc_b + ((uint32_t)wcol + (ln & 31)) * (uint32_t)esz;
       const int lo = ed.row_lo, hi = ed.row_hi;
       const bool part = lo > 0 || hi < BM;
       // a contraction half of a split tile adds into C (branch outside the
@@ -873,8 +885,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
-            if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
-            char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
+            if (part && (row < lo || row >= hi)) continue;
+            char* rbase =
+                (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               (void)__builtin_amdgcn_global_atomic_fadd_f32(
@@ -882,25 +895,42 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
           }
         }
       } else {
+        // whole tiles take a loop without the row check (a tile's rows are
+        // all stored unless it is a tail tile, part); the check is uniform:
+        // rows R and R + 4 of one store lie in one 8-row group, and row_lo
+        // and row_hi are multiples of 128
+        auto store_rows = [&](auto check) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
-            if (part && (row + 4 * fg < lo || row + 4 * fg >= hi)) continue;
-            char* rbase = ed.c + (int64_t)row * ldc_b + lane_off;
+            for (int r = 0; r < 16; ++r) {
+              const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+              if (decltype(check)::value && (row < lo || row >= hi)) continue;
+              char* rbase =
+                  (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
+              if (OUT_BF16) {
+                // two columns 32 apart per conversion (one V_CVT_PK_BF16_F32)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (OUT_BF16)
-                __builtin_nontemporal_store(
-                    (uint16_t)f32_to_bf16(acc[i][j][r]),
-                    (__attribute__((address_space(1))) uint16_t*)(rbase + j * 32 * 2));
-              else
-                __builtin_nontemporal_store(
-                    acc[i][j][r], (__attribute__((address_space(1))) float*)(rbase + j * 32 * 4));
+                for (int j = 0; j < 4; j += 2) {
+                  const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j + 1][r]);
+                  __builtin_nontemporal_store(
+                      (uint16_t)pk, (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64));
+                  __builtin_nontemporal_store(
+                      (uint16_t)(pk >> 16),
+                      (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64 + 64));
+                }
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  __builtin_nontemporal_store(
+                      acc[i][j][r], (__attribute__((address_space(1))) float*)(rbase + j * 128));
+              }
             }
           }
-        }
+        };
+        // (one loop for the SwiGLU kernel, whose epilogue is long enough)
+        if (SWIGLU || part) store_rows(std::true_type{});
+        else store_rows(std::false_type{});
       }
       if (SWIGLU) {
         // SwiGLU + quantize of the tile: a = silu(gate) * up for the 256 x 128
@@ -925,8 +955,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last stage
         __syncthreads();                      // every wave's: the stage slots are free
         uint8_t* sub = smem + (2 * wn + wm_u) * kLdsBytesBf16;
-        uint32_t ln;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
         const int lane_lds = (int)(4 * (ln >> 5) * 256 + 2 * (ln & 31));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -973,20 +1001,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         }
       }
     }
-    // wgrad (one expert's tokens: short contractions, so the epilogue weighs
-    // more; 6 % faster than one register per store).  Accumulating into C,
-    // an expert without tokens (nk == 0) leaves its C untouched, and the old
-    // values are loaded 16 at a time (one 4-row block of every fragment)
-    // before they are added: the wait for a load also waits for every store
-    // issued before it, so loading one value at a time would serialise.
-    // Registers 4b..4b+3 of a quad of lanes (4 consecutive columns) hold a
-    // 4 x 4 block of C; a DPP transpose inside the quad leaves lane q of it
-    // with row 8b + 4 (l/32) + q, its 4 columns in registers 0..3, so one
-    // 16-byte store per 4 registers writes, per instruction, 8 rows of 32
-    // consecutive columns: whole 128-byte lines (fp32), 4x fewer store
-    // instructions than one register at a time.  The row part of the address
-    // is wave-uniform (scalar base); the lane part is a 32-bit offset.
-    else if (!ACCUM || nk > 0) {
+    // wgrad accumulating into C (fp32): an expert without tokens (nk == 0)
+    // leaves its C untouched, and the old values are loaded 16 at a time
+    // (one 4-row block of every fragment) before they are added: the wait
+    // for a load also waits for every store issued before it, so loading one
+    // value at a time would serialise.  Registers 4b..4b+3 of a quad of
+    // lanes (4 consecutive columns) hold a 4 x 4 block of C; a DPP transpose
+    // inside the quad leaves lane q of it with row 8b + 4 (l/32) + q, its 4
+    // columns in registers 0..3, so one 16-byte load and store per 4
+    // registers cover, per instruction, 8 rows of 32 consecutive columns:
+    // whole 128-byte lines, 4x fewer loads than one register at a time.  The
+    // row part of the address is wave-uniform (scalar base); the lane part is
+    // a 32-bit offset.
+    else if (nk > 0) {
+      static_assert(!ACCUM || !OUT_BF16, "the accumulating wgrad adds into fp32");
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
       // per-lane values derived here from the hardware lane id (volatile
@@ -995,69 +1023,48 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       // left
       uint32_t ln;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-      const uint32_t q4 = ln & 3;               // row of the 4 x 4 block after the transpose
       const uint32_t cq = (ln & 31) >> 2;       // column quad of the 32-column fragment
       const bool odd = (ln & 1) != 0, hi2 = (ln & 2) != 0;
-      const uint32_t my_row = 4 * (ln >> 5) + q4;   // within an 8-row group
+      const uint32_t my_row = 4 * (ln >> 5) + (ln & 3);   // within an 8-row group
       // 32-bit lane offset (7 rows of at most a few hundred KB plus a column)
       const uint32_t lane_off =
           my_row * (uint32_t)ldc_b + (uint32_t)(wn * WT) * (uint32_t)esz + 4 * cq * (uint32_t)esz;
-      const int lo = ed.row_lo, hi = ed.row_hi;
-      const bool part = lo > 0 || hi < BM;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 old[4][4];
-        if (ACCUM) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int row = wm_u * WT + 32 * i + 8 * b;
-            const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
+        for (int b = 0; b < 4; ++b) {
+          const int row = wm_u * WT + 32 * i + 8 * b;
+          const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              old[b][j] = __builtin_nontemporal_load(
-                  (__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4));
-          }
+          for (int j = 0; j < 4; ++j)
+            old[b][j] = __builtin_nontemporal_load(
+                (__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4));
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
-          const bool ok = !part || (row + (int)my_row >= lo && row + (int)my_row < hi);
-          // scalar row base + 32-bit lane offset (the scalar-base store form)
           char* rbase = (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
             float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
             quad_transpose(v0, v1, v2, v3, odd, hi2);
-            if (ACCUM) {
-              v0 += old[b][j].x;
-              v1 += old[b][j].y;
-              v2 += old[b][j].z;
-              v3 += old[b][j].w;
-            }
-            if (!ok) continue;
-            if (OUT_BF16) {
-              // an ordinary store: one instruction covers 64 bytes of each
-              // row, half a line; through L2 the two halves merge, while
-              // non-temporal they reached memory as partial lines (1.46x
-              // the written bytes, fused-MLP FC2 wgrad 0.50 -> 0.47 ms)
-              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-              *(__attribute__((address_space(1))) u32x2*)(rbase + j * 32 * 2) =
-                  u32x2{f32_to_bf16(v0) | (f32_to_bf16(v1) << 16),
-                        f32_to_bf16(v2) | (f32_to_bf16(v3) << 16)};
-            } else {
-              __builtin_nontemporal_store(f32x4{v0, v1, v2, v3},
-                  (__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4));
-            }
+            v0 += old[b][j].x;
+            v1 += old[b][j].y;
+            v2 += old[b][j].z;
+            v3 += old[b][j].w;
+            __builtin_nontemporal_store(f32x4{v0, v1, v2, v3},
+                (__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4));
           }
         }
       }
     }
     if (next >= up.nunits) break;
-    // the store loops above issue one operation per register (M-grouped: 256
-    // per wave, every row inside the tile) or per 4 registers (K-grouped: 64
-    // stores, plus 64 loads when accumulating)
+    // the store loops above issue one operation per register (256 per wave
+    // for every row inside the tile) or, accumulating, 64 loads and 64
+    // stores
     // (SwiGLU: the next tile's copies were issued last; wait for them)
     if (SWIGLU || !(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

@@ -242,6 +242,43 @@ def _run_steps(launches, steps, warmup):
     return start.elapsed_time(stop) / steps, per
 
 
+def vendor_reference(m, n, k, steps):
+    """The vendor BLAS (hipBLASLt, through torch._scaled_mm) on one dense
+    GEMM with the flops of one grouped launch of the headline workload
+    (M = all tokens, N, K): MXFP8 with E8M0 block scales, and FP8 with one
+    scale per tensor.  Context for the grouped kernel's rate, not part of
+    the path; an entry holds the error text where this build lacks a form."""
+    import torch
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    a = (torch.randn(m, k, device=dev, generator=gen) * 0.5).to(torch.float8_e4m3fn)
+    b = (torch.randn(n, k, device=dev, generator=gen) * 0.5).to(torch.float8_e4m3fn)
+    flops = 2.0 * m * n * k
+    out = {"shape": [m, n, k], "library": "hipBLASLt via torch._scaled_mm"}
+
+    def run(name, fn):
+        try:
+            ms = _time_outside(fn, steps)
+            out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        except Exception as e:  # noqa: BLE001 - reported, not raised
+            out[name] = f"unavailable: {type(e).__name__}: {str(e)[:160]}"
+
+    e8m0 = getattr(torch, "float8_e8m0fnu", None)
+    if e8m0 is not None:
+        sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev).view(e8m0)
+        sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev).view(e8m0)
+        run("mxfp8_bf16_out", lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb,
+                                                        out_dtype=torch.bfloat16))
+        del sa, sb
+    one = torch.ones((), device=dev)
+    run("fp8_per_tensor_fp32_out", lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one,
+                                                            out_dtype=torch.float32))
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def _gemm_roofline_ms(flops, bytes_):
     """Time bound of one GEMM launch: the larger of its flops at the MFMA peak
     and its algorithmic bytes at the HBM peak."""
@@ -935,6 +972,7 @@ def main():
             others[name] = fn(o_steps, o_warm)
             torch.cuda.empty_cache()
         res["other_workloads"] = others
+        res["vendor_reference"] = vendor_reference(t, n, k, o_steps)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

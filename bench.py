@@ -38,7 +38,7 @@ tiles dynamically unless 1 expert in 8 or more has no token.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
        python bench.py --only NAME           (one of the other workloads alone)
        python bench.py --calibrate-copy      (copy of 1 GiB, for counter scaling)
-       python bench.py --summarize trace|traffic ...   (profiles/ tables from rocprofv3 CSVs)
+       python bench.py --summarize trace|traffic|mfma|cache ...   (profiles/ tables from rocprofv3 CSVs)
 """
 
 import argparse
@@ -679,6 +679,55 @@ Per launch: GRBM_GUI_ACTIVE is summed over the 8 XCDs, so divided by 8 and by th
 """
 
 
+def summarize_cache(pmc_dirs, title, commands, cycles=None):
+    """Markdown of --pmc runs (one directory each; launches matched by label
+    in dispatch order) with TCC_HIT_sum / TCC_MISS_sum, TCC_EA0_RDREQ_sum /
+    TCC_EA0_RDREQ_LEVEL_sum, SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES and TA_BUSY_avr
+    / GRBM_GUI_ACTIVE: per launch label the L2 hit rate, the mean latency of
+    the reads that miss L2 (Little's law: outstanding requests summed per
+    cycle over requests), the share of wave cycles spent waiting, and the
+    texture-address unit's busy share."""
+    import collections
+    import statistics as st
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in pmc_dirs:
+        rows = _csv(os.path.join(d, "p_counter_collection.csv"))
+        by = collections.OrderedDict()
+        for r in rows:
+            e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+        labels = _labels([e["name"] for e in by.values()], cycles)
+        for e, lab in zip(by.values(), labels):
+            if "TCC_HIT_sum" in e:
+                per[lab]["hit"].append(e["TCC_HIT_sum"] / (e["TCC_HIT_sum"] + e["TCC_MISS_sum"]))
+            if "TCC_EA0_RDREQ_sum" in e and e["TCC_EA0_RDREQ_sum"] > 0:
+                per[lab]["lat"].append(e["TCC_EA0_RDREQ_LEVEL_sum"] / e["TCC_EA0_RDREQ_sum"])
+            if "SQ_WAVE_CYCLES" in e:
+                per[lab]["wait"].append(e["SQ_WAIT_INST_ANY"] / e["SQ_WAVE_CYCLES"])
+            if "TA_BUSY_avr" in e:
+                per[lab]["ta"].append(e["TA_BUSY_avr"] / (e["GRBM_GUI_ACTIVE"] / 8))
+    f = lambda v, fmt: "-" if not v else fmt.format(st.mean(v))  # noqa: E731
+    tab = ["| launch | L2 hit rate | mean latency of L2-miss reads, cycles | wave cycles "
+           "waiting | address unit busy |", "|---|---|---|---|---|"]
+    for lab, v in per.items():
+        tab.append(f"| {lab} | {f([100 * x for x in v['hit']], '{:.0f} %')} | "
+                   f"{f(v['lat'], '{:.0f}')} | {f([100 * x for x in v['wait']], '{:.0f} %')} | "
+                   f"{f([100 * x for x in v['ta']], '{:.0f} %')} |")
+    cmd = "\n".join(commands)
+    return f"""# {title}
+
+Counters, each group in a run of its own (from the repository root, one MI355X):
+
+```
+{cmd}
+```
+
+""" + "\n".join(tab) + """
+
+Per launch label (mean over its launches): L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum); mean latency of the reads that miss L2 = TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum (the outstanding read requests of the L2 to the memory fabric, summed per cycle, over the requests: Little's law, in L2 cycles); wave cycles waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waits on memory counters and barriers); address unit busy = TA_BUSY_avr over the active cycles of one XCD (GRBM_GUI_ACTIVE / 8).  Written by `python bench.py --summarize cache ...`.
+"""
+
+
 def quantize_source_hash():
     h = hashlib.sha256()
     for rel in ["moe_expert_grouped_group_amd/csrc/quantize.hip",
@@ -694,12 +743,13 @@ def quantize_source_hash():
 
 def summarize_main(argv):
     ap = argparse.ArgumentParser(prog="bench.py --summarize")
-    ap.add_argument("kind", choices=["trace", "traffic", "mfma"])
+    ap.add_argument("kind", choices=["trace", "traffic", "mfma", "cache"])
     ap.add_argument("--out", required=True, help="markdown file to write")
     ap.add_argument("--title", required=True)
     ap.add_argument("--command", action="append", default=[],
                     help="the rocprofv3 command line(s) the CSVs came from (quoted in the file)")
-    ap.add_argument("--dir", help="trace, mfma: the rocprofv3 output directory")
+    ap.add_argument("--dir", action="append", default=[],
+                    help="trace, mfma: the rocprofv3 output directory (cache: one per run)")
     ap.add_argument("--note", default="")
     ap.add_argument("--cycle", action="append", default=[],
                     help="trace: KERNEL=name1,name2,... names for successive launches of KERNEL")
@@ -711,9 +761,11 @@ def summarize_main(argv):
     a = ap.parse_args(argv)
     cycles = {c.split("=")[0]: c.split("=")[1].split(",") for c in a.cycle}
     if a.kind == "trace":
-        md = summarize_trace(a.dir, a.title, a.command, a.note, cycles or None)
+        md = summarize_trace(a.dir[0], a.title, a.command, a.note, cycles or None)
     elif a.kind == "mfma":
-        md = summarize_mfma(a.dir, a.title, a.command, cycles or None)
+        md = summarize_mfma(a.dir[0], a.title, a.command, cycles or None)
+    elif a.kind == "cache":
+        md = summarize_cache(a.dir, a.title, a.command, cycles or None)
     else:
         md = summarize_traffic(a.workload, a.cal_fetch, a.cal_write, a.fetch, a.write, a.title,
                                a.command, cycles or None)

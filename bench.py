@@ -55,8 +55,8 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "moe8_h4096_f14336"
 PEAK_MXFP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-GEMM_SOURCES = ["moe_expert_grouped_group_amd/csrc/gemm.hip",
-                "moe_expert_grouped_group_amd/csrc/mx_device.h"]
+GEMM_SOURCE = "moe_expert_grouped_group_amd/csrc/gemm.hip"
+QUANTIZE_SOURCE = "moe_expert_grouped_group_amd/csrc/quantize.hip"
 COPY_BYTES = 1 << 30
 
 
@@ -83,12 +83,32 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_hash():
-    """sha256 of the GEMM sources with comments and whitespace removed, so
-    that only a change of the code itself retires the stored counters."""
+def _source_files(rel):
+    """`rel` and every local header it includes (#include "...", followed
+    recursively), in a fixed order."""
+    seen, order = set(), []
+
+    def visit(path):
+        path = os.path.normpath(path)
+        if path in seen:
+            return
+        seen.add(path)
+        order.append(path)
+        with open(os.path.join(ROOT, path)) as f:
+            for inc in re.findall(r'^\s*#include\s+"([^"]+)"', f.read(), re.M):
+                visit(os.path.join(os.path.dirname(path), inc))
+
+    visit(rel)
+    return order
+
+
+def _source_hash(rel):
+    """sha256 of a kernel source and the local headers it includes, with
+    comments and whitespace removed, so that only a change of the code itself
+    retires the counters taken on it."""
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
-        with open(os.path.join(ROOT, rel)) as f:
+    for path in _source_files(rel):
+        with open(os.path.join(ROOT, path)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
@@ -96,10 +116,15 @@ def gemm_source_hash():
     return h.hexdigest()
 
 
-def stored_traffic(workload):
+def gemm_source_hash():
+    return _source_hash(GEMM_SOURCE)
+
+
+def stored_traffic(workload, profiles_dir=None):
     """HBM bytes per GEMM launch from the counter summary, or None when the
     summary is missing or was taken on a different GEMM source."""
-    path = os.path.join(ROOT, "profiles", f"grouped_gemm_hbm_traffic_{workload}.md")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                        f"grouped_gemm_hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -729,16 +754,7 @@ Per launch label (mean over its launches): L2 hit rate = TCC_HIT_sum / (TCC_HIT_
 
 
 def quantize_source_hash():
-    h = hashlib.sha256()
-    for rel in ["moe_expert_grouped_group_amd/csrc/quantize.hip",
-                "moe_expert_grouped_group_amd/csrc/mx_device.h",
-                "moe_expert_grouped_group_amd/csrc/mx_convert.h"]:
-        with open(os.path.join(ROOT, rel)) as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", "", text)
-        h.update(re.sub(r"\s+", "", text).encode())
-    return h.hexdigest()
+    return _source_hash(QUANTIZE_SOURCE)
 
 
 def summarize_main(argv):

@@ -411,9 +411,10 @@ def bench_fused_mlp(steps, warmup):
         ("quant_requant_x", lambda: mx.group_quantize_requant(x, out=xo)),
         ("quant_w1", lambda: mx.group_quantize(w1, R | C, out=w1o)),
         ("quant_w2", lambda: mx.group_quantize(w2, R | C, out=w2o)),
-        ("fc1_fprop", lambda: gemm("NT", xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale,
-                                   ms, t, n2, k, bf, h)),
-        ("swiglu_quant", lambda: mx.swiglu_quantize(h, R | C, out=ao)),
+        # FC1 with the SwiGLU + quantize in its epilogue: h for the backward
+        # and both MXFP8 copies of a = silu(gate) * up for FC2, one launch
+        ("fc1_swiglu_quant", lambda: mx.grouped_gemm_swiglu_quantize(
+            xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale, ms, t, f, k, h=h, out=ao)),
         ("fc2_fprop", lambda: gemm("NT", ao.row_data, ao.row_scale, w2o.row_data, w2o.row_scale,
                                    ms, t, k, f, bf, y)),
         ("quant_requant_dy", lambda: mx.group_quantize_requant(dout, out=dyo)),
@@ -430,11 +431,6 @@ def bench_fused_mlp(steps, warmup):
                                    ms, t, n2, k, bf, dw1, workspace=gws)),
     ]
     ms_step, per = _run_steps(launches, steps, warmup)
-    # FC1 with the SwiGLU + quantize in its epilogue (same h and bytes as
-    # fc1_fprop + swiglu_quant), timed outside the step
-    fused_ms = _time_outside(lambda: mx.grouped_gemm_swiglu_quantize(
-        xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale, ms, t, f, k, h=h, out=ao),
-        steps)
     flops = 3 * 2.0 * t * k * n2 + 3 * 2.0 * t * f * k
     gemm_ms = sum(v for nm, v in per.items() if nm.startswith("fc"))
     return {
@@ -445,11 +441,44 @@ def bench_fused_mlp(steps, warmup):
         "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 2),
         "gemm_frac_of_peak": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
         "kernel_ms": {nm: round(v, 4) for nm, v in per.items()},
-        "fc1_swiglu_quantize_fused_ms": round(fused_ms, 4),
-        "note": "the step launches FC1 and swiglu_quant separately; "
-                "fc1_swiglu_quantize_fused_ms is the one-launch form "
-                "(mxfp8_grouped_gemm_swiglu_quantize), timed outside the step",
+        "note": "fc1_swiglu_quant is FC1 with the SwiGLU + row/column MXFP8 quantize in its "
+                "epilogue (mxfp8_grouped_gemm_swiglu_quantize); the GEMM time includes it",
     }
+
+
+def bench_fc1_swiglu(steps, warmup):
+    """FC1 of the fused MLP (83968 tokens, 3072 -> 2 x 1024, 64 experts) as
+    one launch with the SwiGLU + quantize epilogue, against the two launches
+    it replaces (the bf16 FC1 GEMM, then swiglu_quantize of its output)."""
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    del warmup
+    w = wl.make("nemotron_proxy_mlp")
+    t, k, n2 = w.tokens, w.hidden, w.ffn
+    f = n2 // 2
+    ms = torch.from_numpy(w.m_splits).cuda()
+    R, C = mx.ROWWISE, mx.COLWISE
+    xo = mx.group_quantize(w.tensors["x"].cuda(), R)
+    w1o = mx.group_quantize(w.tensors["w"].cuda(), R | C)
+    del w
+    h = torch.empty(t, n2, dtype=torch.bfloat16, device="cuda")
+    ao = mx.swiglu_quantize(torch.zeros_like(h), R | C)
+    fc1 = lambda: mx.grouped_gemm("NT", xo.row_data, xo.row_scale, w1o.row_data,  # noqa: E731
+                                  w1o.row_scale, ms, t, n2, k, torch.bfloat16, h)
+    sq = lambda: mx.swiglu_quantize(h, R | C, out=ao)  # noqa: E731
+    fused = lambda: mx.grouped_gemm_swiglu_quantize(  # noqa: E731
+        xo.row_data, xo.row_scale, w1o.row_data, w1o.row_scale, ms, t, f, k, h=h, out=ao)
+    fc1_ms = _time_outside(fc1, steps)
+    sq_ms = _time_outside(sq, steps)
+    fused_ms = _time_outside(fused, steps)
+    return {"tokens": t, "hidden": k, "fc1_out": n2, "fc1_ms": round(fc1_ms, 4),
+            "swiglu_quant_ms": round(sq_ms, 4), "unfused_ms": round(fc1_ms + sq_ms, 4),
+            "fused_ms": round(fused_ms, 4),
+            "note": "same h and MXFP8 bytes either way (tests); the fused MLP step uses the "
+                    "fused launch"}
 
 
 def bench_group_quantize(steps, warmup):
@@ -541,6 +570,8 @@ def algorithmic_bytes(workload):
         k, n2, f = 3072, 2048, 1024
         return {
             "fc1_fprop": t * k * sc + g * n2 * k * sc + t * n2 * 2,
+            # FC1 with the SwiGLU + quantize epilogue: h and both copies of a
+            "fc1_swiglu_quant": t * k * sc + g * n2 * k * sc + t * n2 * 2 + 2 * t * f * sc,
             "fc2_fprop": t * f * sc + g * k * f * sc + t * k * 2,
             "fc2_dgrad": t * k * sc + g * k * f * sc + t * f * 2,
             "fc1_dgrad": t * n2 * sc + g * n2 * k * sc + t * k * 2,
@@ -791,6 +822,7 @@ def summarize_main(argv):
 
 
 OTHERS.update({"skewed_dsv3": bench_skewed_linear, "nemotron_proxy_mlp": bench_fused_mlp,
+               "fc1_swiglu_quantize": bench_fc1_swiglu,
                "group_quantize_131072x7168": bench_group_quantize})
 
 

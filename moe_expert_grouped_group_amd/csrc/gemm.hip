@@ -488,8 +488,6 @@ __device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const Exper
 template <bool KGROUPED, bool OUT_BF16, bool ACCUM = false, bool SWIGLU = false>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(!SWIGLU || (!KGROUPED && OUT_BF16 && !ACCUM), "SwiGLU epilogue: forward, bf16");
-  static_assert(4 * kLdsBytesBf16 <= kSlots * kStageBytes + 2 * kScaleBuf,
-                "SwiGLU epilogue: four staged 128 x 128 bf16 tiles fit the stage buffers");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
   __shared__ int32_t next_lds;          // dynamic order: the next tile, from thread 0
@@ -529,8 +527,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     const int64_t wrow = (int64_t)((wave * 64) % d.rows_avail);
     a_base = uniform_ptr(d.a + wrow * p.lda);
     sa_base = uniform_ptr(d.sa + wrow * p.ldsa);
-    // SwiGLU: waves 2 and 3 copy the up rows, F rows after the gate rows
-    const int64_t brow = (int64_t)wave * 64 + (SWIGLU && wave >= 2 ? p.f - BN / 2 : 0);
+    // SwiGLU: LDS B rows [64 w, 64 w + 64) hold the gate rows (w even) or the
+    // up rows (w odd, F rows further on) of the tile's columns 64 (w / 2)..;
+    // so the MFMA wave wn holds gate columns 64 wn.. in fragments 0, 1 and
+    // the matching up columns in fragments 2, 3
+    const int64_t brow = SWIGLU ? (int64_t)(wave & 1) * p.f + (int64_t)(wave >> 1) * 64
+                                : (int64_t)wave * 64;
     b_base = uniform_ptr(d.b + brow * p.ldb);
     sb_base = uniform_ptr(d.sb + brow * p.ldsb);
     s_nblk = d.nblk;
@@ -829,10 +831,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     }
     TileDesc nxt;
     nxt.nk = 0;
-    // (SwiGLU: the epilogue uses the LDS, so the next tile's copies wait
-    // until after it)
-    if (!SWIGLU && next < up.nunits) {
-      nxt = describe_unit<KGROUPED>(p, &table, up, next, esz);
+    if (next < up.nunits) {
+      nxt = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
       setup(nxt);
@@ -865,8 +865,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     if (!KGROUPED || !ACCUM) {
       const int64_t ldc_b = p.ldc * esz;
       const int wm_u = __builtin_amdgcn_readfirstlane(wm);
-      // SwiGLU: the up wave's columns lie F after the gate wave's
-      const int64_t wcol = SWIGLU ? wn * p.f : wn * WT;
+      // SwiGLU: the wave's gate columns start 64 wn into the tile; its up
+      // columns (fragments 2, 3) lie F further on
+      const int64_t wcol = SWIGLU ? 64 * wn : wn * WT;
       // the lane's part of the store address, formed here from the hardware
       // lane id (volatile: not hoisted and kept through the K loop) as a
       // 32-bit offset to a scalar row base: the scalar-base store form, with
@@ -913,11 +914,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < 4; j += 2) {
                   const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j + 1][r]);
+                  const int64_t jo = SWIGLU && j == 2 ? 2 * p.f : j * 64;
                   __builtin_nontemporal_store(
-                      (uint16_t)pk, (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64));
+                      (uint16_t)pk, (__attribute__((address_space(1))) uint16_t*)(rbase + jo));
                   __builtin_nontemporal_store(
                       (uint16_t)(pk >> 16),
-                      (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64 + 64));
+                      (__attribute__((address_space(1))) uint16_t*)(rbase + jo + 64));
                 }
               } else {
 #pragma unroll
@@ -932,72 +934,112 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         if (SWIGLU || part) store_rows(std::true_type{});
         else store_rows(std::false_type{});
       }
-      if (SWIGLU) {
-        // SwiGLU + quantize of the tile: a = silu(gate) * up for the 256 x 128
-        // gate/up pairs (gate in waves wn = 0, up in waves wn = 1, same rows
-        // and columns).  Every wave stages its bf16-rounded h block in LDS as
-        // a 128 x 128 tile in the layout of the streaming quantize kernels
-        // (gate tiles 0, 1 for rows 0..127 and 128..255 of the copied rows, up
-        // tiles 2, 3); then all 256 threads form a as swiglu_pair does and
-        // quantize it row-wise from registers, writing a over the gate tile,
-        // and run the column-wise pass on it: the bytes of
-        // mxfp8_swiglu_quantize on the h written above.
-        // MFMA layout: register r of fragment (i, j) in lane l is row
-        // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 j + l % 32 of the
-        // wave's 128 x 128 block; (row >> 4) = 2 i + (r >= 8), so the lane's
-        // part of the LDS offset is 4 (l / 32) rows and 2 (l % 32) bytes.
-        // The accumulators as the compiler must re-read them: otherwise it
-        // keeps the bf16 values of the h stores above live until here.
+      if (SWIGLU && (p.q_row != nullptr || p.q_col != nullptr) && 128 * wm_u >= lo &&
+          128 * wm_u + 128 <= hi) {
+        // SwiGLU + quantize from registers.  Fragments (i, jj) and (i, jj + 2)
+        // hold gate and up for the same 32 x 32 block (rows 32 i.. of the
+        // wave's 128, columns 64 wn + 32 jj.. of the tile's gate columns):
+        // a = silu(gate) * up as swiglu_pair forms it from the bf16-rounded
+        // h.  Column-wise: lane l holds rows 8 g + 4 (l / 32) + (0..3) of
+        // column l % 32 (g = r / 4), so a 32-token block is 16 registers of
+        // lanes l and l ^ 32; after two words change hands each lane stores 16
+        // consecutive tokens.  Row-wise: a DPP transpose inside each quad
+        // gives lane q four consecutive columns of row 8 b + 4 (l / 32) + q;
+        // the row's 32-column block is the eight quads of the half-wave.
+        // The encode is the streaming kernels' (scaled conversion of bf16
+        // pairs with the block's E8M0 byte, saturated), so the bytes equal
+        // mxfp8_swiglu_quantize of the h written above.
+        const int64_t F = p.f, T = p.rows;
+        const uint32_t half = ln >> 5, c = ln & 31;
+        const int64_t fc0 = (int64_t)ed.nt * 128 + 64 * wn;   // the wave's first a column
+        const int64_t tok0 = ed.m0c + 128 * wm_u;              // the wave's first token
+        // per-lane parts of the addresses (32-bit)
+        const uint32_t col_l = c * (uint32_t)T + 16 * half;
+        const uint32_t scol_l = c * (uint32_t)(T / 32);
+        const uint32_t row_l = (ln >> 1) * (uint32_t)F + 16 * (ln & 1);
+        const uint32_t srow_l = (ln >> 1) * (uint32_t)(F / 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t sbytes = 0;   // column-wise scale bytes of blocks i = 0..3
 #pragma unroll
-          for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last stage
-        __syncthreads();                      // every wave's: the stage slots are free
-        uint8_t* sub = smem + (2 * wn + wm_u) * kLdsBytesBf16;
-        const int lane_lds = (int)(4 * (ln >> 5) * 256 + 2 * (ln & 31));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < 4; ++i) {
+            // gate and up rounded to bf16 as the h stores round them (two
+            // values per V_CVT_PK_BF16_F32), a rounded as swiglu_pair rounds it
+            uint32_t a[16];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-              // registers r, r + 1: rows R, R + 1 of one column
-              const int row = 32 * i + 8 * (r / 4) + (r % 4);
-              const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
-              uint8_t* e = sub + lds_off_bf16(row, 64 * j) + lane_lds;
-              *reinterpret_cast<uint16_t*>(e) = (uint16_t)pk;
-              *reinterpret_cast<uint16_t*>(e + 256) = (uint16_t)(pk >> 16);
+              const uint32_t gp = pack_bf16x2(acc[i][jj][r], acc[i][jj][r + 1]);
+              const uint32_t up = pack_bf16x2(acc[i][jj + 2][r], acc[i][jj + 2][r + 1]);
+              a[r] = f32_to_bf16(silu_f(__uint_as_float(gp << 16)) * __uint_as_float(up << 16));
+              a[r + 1] = f32_to_bf16(silu_f(__uint_as_float(gp & 0xFFFF0000u)) *
+                                     __uint_as_float(up & 0xFFFF0000u));
             }
-        __syncthreads();
-        // the thread index from the hardware here (volatile: not hoisted),
-        // so that the passes' per-thread offsets are formed here and not
-        // kept in registers through the K loop
-        const int tq = (int)(ln + 64 * (uint32_t)wave);
-        const int64_t k0 = (int64_t)ed.nt * 128;
-        // sub-tiles wholly inside the tile's rows (row_lo and row_hi are
-        // multiples of 128: expert runs are)
+            if (p.q_col != nullptr) {
+              uint32_t m = 0;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          if (128 * s2 < lo || 128 * s2 + 128 > hi) continue;
-          swiglu_rowwise_pass(smem + s2 * kLdsBytesBf16, smem + (2 + s2) * kLdsBytesBf16, p.f,
-                              k0, ed.m0c + 128 * s2, p.q_row, p.s_row, p.q_col != nullptr, tq);
-        }
-        if (p.q_col != nullptr) {
-          __syncthreads();
+              for (int r = 0; r < 16; ++r) m = max(m, a[r] & 0x7FFFu);
+              {
+                // lanes l and l ^ 32 through V_PERMLANE32_SWAP (lanes 32..63
+                // of the first operand trade with lanes 0..31 of the second)
+                const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+                m = max(m, half ? (uint32_t)sw[0] : (uint32_t)sw[1]);
+              }
+              const uint32_t xb = scale_byte_from_exp(m >> 7);
+              const float sc = e8m0_operand(xb);
+              uint32_t w[4];
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            if (128 * s2 < lo || 128 * s2 + 128 > hi) continue;
-            colwise_pass_bf16<false>(smem + s2 * kLdsBytesBf16, p.rows, p.f, k0,
-                                     ed.m0c + 128 * s2, p.q_col, p.s_col, tq);
+              for (int g = 0; g < 4; ++g)
+                w[g] = cvt4_bf16_e4m3(a[4 * g] | (a[4 * g + 1] << 16),
+                                      a[4 * g + 2] | (a[4 * g + 3] << 16), sc);
+              // w[g]: tokens 8 g + 4 half .. + 3; lanes l and l ^ 32 trade two
+              // words so that lane l holds tokens 0..15 and lane l ^ 32 16..31
+              // one swap each: lane l < 32 receives the partner's w[0] / w[1],
+              // lane l + 32 the partner's w[2] / w[3]
+              const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+              const uint32_t y0 = half ? (uint32_t)s0[0] : (uint32_t)s0[1];
+              const uint32_t y1 = half ? (uint32_t)s1[0] : (uint32_t)s1[1];
+              const u32x4 o = half ? u32x4{y0, w[2], y1, w[3]} : u32x4{w[0], y0, w[1], y1};
+              uint8_t* qb = (uint8_t*)uniform_ptr(p.q_col + (fc0 + 32 * jj) * T + tok0 + 32 * i);
+              *(__attribute__((address_space(1))) u32x4*)(qb + col_l) = o;
+              sbytes |= xb << (8 * i);
+            }
+            if (p.q_row != nullptr) {
+              // row-wise through this wave's 2 KiB of the second scale buffer
+              // (free until the next tile's K loop loads scale group 1): the
+              // 32 x 32 block row-major, then lane l reads half l % 2 of row
+              // l / 2 (16 values of one row: one scale, 16 codes, one store)
+              uint16_t* xw = reinterpret_cast<uint16_t*>(
+                  smem + kSlots * kStageBytes + kScaleBuf + 2048 * wave);
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                xw[(8 * (r / 4) + 4 * half + (r % 4)) * 32 + c] = (uint16_t)a[r];
+              const u32x4* xr = reinterpret_cast<const u32x4*>(xw + (ln >> 1) * 32 + 16 * (ln & 1));
+              const u32x4 v0 = xr[0], v1 = xr[1];
+              const uint32_t k7 = 0x7FFF7FFFu;
+              uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(v0.x & k7, v0.y & k7),
+                                                max_u16x2(v0.z & k7, v0.w & k7)),
+                                      max_u16x2(max_u16x2(v1.x & k7, v1.y & k7),
+                                                max_u16x2(v1.z & k7, v1.w & k7)));
+              uint32_t m = max(m2 & 0xFFFFu, m2 >> 16);
+              m = max(m, lane_xor1(m));
+              const uint32_t xb = scale_byte_from_exp(m >> 7);
+              const float sc = e8m0_operand(xb);
+              const u32x4 code = u32x4{cvt4_bf16_e4m3(v0.x, v0.y, sc), cvt4_bf16_e4m3(v0.z, v0.w, sc),
+                                       cvt4_bf16_e4m3(v1.x, v1.y, sc), cvt4_bf16_e4m3(v1.z, v1.w, sc)};
+              uint8_t* qb = (uint8_t*)uniform_ptr(p.q_row + (tok0 + 32 * i) * F + fc0 + 32 * jj);
+              *(__attribute__((address_space(1))) u32x4*)(qb + row_l) = code;
+              if ((ln & 1) == 0) {
+                uint8_t* sb = (uint8_t*)uniform_ptr(p.s_row + (tok0 + 32 * i) * (F / 32) +
+                                                    (fc0 + 32 * jj) / 32);
+                *(__attribute__((address_space(1))) uint8_t*)(sb + srow_l) = (uint8_t)xb;
+              }
+            }
           }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __syncthreads();                      // the LDS is free for the next tile's copies
-        if (next < up.nunits) {
-          nxt = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
-          setup(nxt);
-          tile_prologue(nxt.nk);
+          if (p.q_col != nullptr && half == 0) {
+            uint8_t* sb = (uint8_t*)uniform_ptr(p.s_col + (fc0 + 32 * jj) * (T / 32) + tok0 / 32);
+            *(__attribute__((address_space(1))) uint32_t*)(sb + scol_l) = sbytes;
+          }
         }
       }
     }
@@ -1065,8 +1107,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // the store loops above issue one operation per register (256 per wave
     // for every row inside the tile) or, accumulating, 64 loads and 64
     // stores
-    // (SwiGLU: the next tile's copies were issued last; wait for them)
-    if (SWIGLU || !(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
+    if (!(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     tile = next;
     cur = nxt;

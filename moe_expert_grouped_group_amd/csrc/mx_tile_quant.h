@@ -1,5 +1,6 @@
 // Quantize helpers for 128 x 128 bf16 tiles, shared by the streaming quantize
-// kernels and the grouped GEMM's SwiGLU epilogue: row-wise blocks (1 x 32)
+// kernels (and, for the conversions and SwiGLU, the grouped GEMM's SwiGLU
+// epilogue): row-wise blocks (1 x 32)
 // from 16-byte chunks held four lanes to a block, and the column-wise pass
 // (32 x 1 blocks, stored transposed) over a tile staged in LDS.  Both encode
 // with the scaled conversions of mx_convert.h, so every kernel that uses them
@@ -256,37 +257,6 @@ __device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
   const float g0 = bf16_to_f32(gw & 0xFFFFu), g1 = bf16_to_f32(gw >> 16);
   const float u0 = bf16_to_f32(uw & 0xFFFFu), u1 = bf16_to_f32(uw >> 16);
   return f32_to_bf16(silu_f(g0) * u0) | (f32_to_bf16(silu_f(g1) * u1) << 16);
-}
-
-// SwiGLU of a staged 128 x 128 tile pair: gate values in `gl`, up values in
-// `ul` (bf16, layout lds_off_bf16); thread t forms the 16-byte chunks t % 16
-// of rows 16 jj + t / 16 of a = silu(gate) * up (as swiglu_pair), quantizes
-// them row-wise into q_row / s_row (rows t0.., columns k0.. of a [T, K]
-// tensor; skipped when q_row is NULL) as rowwise_pass_bf16 does, and, when
-// keep_a, writes a over the gate values for a column-wise pass.
-__device__ __forceinline__ void swiglu_rowwise_pass(uint8_t* gl, const uint8_t* ul, int64_t K,
-                                                    int64_t k0, int64_t t0,
-                                                    uint8_t* __restrict__ q_row,
-                                                    uint8_t* __restrict__ s_row, bool keep_a,
-                                                    const int tid) {
-  const uint32_t ro = opaque_u32((uint32_t)(tid >> 4) * (uint32_t)K + (tid & 15) * 8);
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int r = 16 * jj + (tid >> 4), cc = tid & 15;
-    const u32x4 g = *reinterpret_cast<const u32x4*>(&gl[lds_off_bf16(r, cc * 16)]);
-    const u32x4 u = *reinterpret_cast<const u32x4*>(&ul[lds_off_bf16(r, cc * 16)]);
-    const uint4 a = make_uint4(swiglu_pair(g.x, u.x), swiglu_pair(g.y, u.y),
-                               swiglu_pair(g.z, u.z), swiglu_pair(g.w, u.w));
-    if (keep_a) *reinterpret_cast<u32x4*>(&gl[lds_off_bf16(r, cc * 16)]) = u32x4{a.x, a.y, a.z, a.w};
-    if (q_row != nullptr) {
-      const uint32_t amax = quad_max(chunk_amax_bits(a));
-      const uint32_t byte = scale_byte_from_exp(amax >> 7);
-      const int64_t rb = t0 * K + k0 + 16 * jj * K;   // uniform
-      *reinterpret_cast<uint2*>(q_row + rb + ro) = encode_chunk(a, byte);
-      const uint32_t bytes4 = gather_blocks4(byte);
-      if ((tid & 15) == 0) *reinterpret_cast<uint32_t*>(s_row + (rb >> 5) + (ro >> 5)) = bytes4;
-    }
-  }
 }
 
 // Row-wise quantize of a staged 128 x 128 bf16 tile (rows t0.., columns k0..

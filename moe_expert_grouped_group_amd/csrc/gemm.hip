@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(!SWIGLU || (!KGROUPED && OUT_BF16 && !ACCUM), "SwiGLU epilogue: forward, bf16");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStageBytes + 2 * kScaleBuf];
   __shared__ ExpertTable table;
-  __shared__ int32_t next_lds;          // dynamic order: the next tile, from thread 0
+  __shared__ int32_t next_lds;          // dynamic order: a tile index, from thread 0
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
@@ -508,8 +508,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   // bytes 4 (i%4) .. 4 (i%4) + 3 of the row's group.
   const int cr = lane >> 3;
   const int cchunk = (lane & 7) ^ cr;
-  const int dr = lane >> 2;
-  const int scol = (lane & 3) * 4;
   const int fr = lane & 31;   // operand row within a 32-row fragment
   const int fg = lane >> 5;   // contraction half of the lane
 
@@ -519,10 +517,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   // rows of the first waves instead; their results are not stored.
   const uint32_t ca = (uint32_t)(cr * p.lda + cchunk * 16);
   const uint32_t cb = (uint32_t)(cr * p.ldb + cchunk * 16);
-  const uint32_t csa = (uint32_t)(dr * p.ldsa);
-  const uint32_t csb = (uint32_t)(dr * p.ldsb);
   const uint8_t *a_base, *b_base, *sa_base, *sb_base;
   int s_nblk;
+  // LDS slot and scale-buffer parity of the current tile's stage 0 and scale
+  // group 0: the copy ring runs on from one tile into the next
+  int spar = 0, gpar = 0;
   auto setup = [&](const TileDesc& d) {
     const int64_t wrow = (int64_t)((wave * 64) % d.rows_avail);
     a_base = uniform_ptr(d.a + wrow * p.lda);
@@ -542,20 +541,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   const uint32_t lds_ring = (uint32_t)(uintptr_t)smem;
   const uint32_t lds_sc = lds_ring + kSlots * kStageBytes;
   // Part j (0..3) of scale group grp (blocks [16 grp, 16 grp + 16) of every
-  // row, MFMA steps [8 grp, 8 grp + 8)) into buffer grp % 2: rows 64 w + 16 j
-  // .. + 16 of A and of B.  In a K-grouped tile the last group may run past
-  // the expert's blocks (s_nblk, a multiple of 4): those lanes re-read the
-  // last valid word.
-  auto scale_part = [&](int grp, int j) {
-    const uint32_t buf = lds_sc + (uint32_t)((grp & 1) * kScaleBuf);
+  // row, MFMA steps [8 grp, 8 grp + 8)) into buffer (grp + gp) % 2: rows
+  // 64 w + 16 j .. + 16 of A and of B.  In a K-grouped tile the last group may
+  // run past the expert's blocks (s_nblk, a multiple of 4): those lanes
+  // re-read the last valid word.
+  auto scale_part = [&](int grp, int j, int gp) {
+    const uint32_t buf = lds_sc + (uint32_t)(((grp + gp) & 1) * kScaleBuf);
+    // lane offsets formed here from the hardware lane id (volatile: not
+    // kept as registers through the loop, where they were spilled)
+    uint32_t ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int dr = (int)(ln >> 2), scol = (int)(ln & 3) * 4;
     const uint32_t col = (uint32_t)(KGROUPED ? max(min(scol, s_nblk - 4 - 16 * grp), 0) : scol);
+    const uint32_t csa = (uint32_t)(dr * p.ldsa), csb = (uint32_t)(dr * p.ldsb);
     dma4(sa_base + (int64_t)j * 16 * p.ldsa + 16 * grp, csa + col,
          buf + (wave * 64 + j * 16) * kScaleRow);
     dma4(sb_base + (int64_t)j * 16 * p.ldsb + 16 * grp, csb + col,
          buf + kScOffB + (wave * 64 + j * 16) * kScaleRow);
   };
   // Copies of stage st (contraction bytes [128 st, 128 st + 128)) into LDS
-  // slot st % 2, part by part (rows 64 w + 8 j .. + 8, j = 0..7): a scalar
+  // slot (st + sp) % 2, part by part (rows 64 w + 8 j .. + 8, j = 0..7): a scalar
   // source pointer and LDS destination per operand, each advanced by one
   // part after its copy.
   struct StageCopy {
@@ -564,11 +569,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     uint32_t la, lb;
   };
   const int64_t a_part = 8 * p.lda, b_part = 8 * p.ldb;
-  auto stage_copy = [&](int st) {
+  auto stage_copy = [&](int st, int sp) {
     StageCopy c;
     c.ak = a_base + (int64_t)st * BK;
     c.bk = b_base + (int64_t)st * BK;
-    c.la = lds_ring + (uint32_t)((st % kSlots) * kStageBytes) + (uint32_t)(wave * 64 * BK);
+    c.la = lds_ring + (uint32_t)(((st + sp) % kSlots) * kStageBytes) + (uint32_t)(wave * 64 * BK);
     c.lb = c.la + kOffB;
     return c;
   };
@@ -605,9 +610,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     uint32_t a0, a1, b0, b1, sa, sb;
   };
   auto step_read = [&](int kt) {
-    const uint32_t data = lds_ring + (uint32_t)(((kt >> 1) % kSlots) * kStageBytes) +
+    const uint32_t data = lds_ring + (uint32_t)((((kt >> 1) + spar) % kSlots) * kStageBytes) +
                           ((kt & 1) ? rH : 0u);
-    const uint32_t scale = lds_sc + (uint32_t)(((kt / kScaleSteps) & 1) * kScaleBuf) +
+    const uint32_t scale = lds_sc + (uint32_t)((((kt / kScaleSteps) + gpar) & 1) * kScaleBuf) +
                            (uint32_t)(2 * (kt % kScaleSteps));
     StepRead r;
     r.a0 = opaque(data + rA);
@@ -626,21 +631,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     bf[set][j] = lds_frag(r.b0 + j * 32 * BK, r.b1 + j * 32 * BK);
     bs[set][j] = lds_byte(r.sb + j * 32 * kScaleRow);
   };
-  // First copies of a tile: stages 0 (with scale group 0) and 1.
-  auto tile_prologue = [&](int nk) {
+  // First copies of a tile: stages 0 (with scale group 0) and 1, into slots
+  // sp, sp ^ 1 and scale buffer gp.
+  auto tile_prologue = [&](int nk, int sp, int gp) {
     __builtin_amdgcn_sched_barrier(0);
     if (nk > 0) {
-      StageCopy c0 = stage_copy(0);
+      StageCopy c0 = stage_copy(0, sp);
 #pragma unroll
       for (int j = 0; j < kDmaHalf; ++j) {
         copy_a(c0);
         copy_b(c0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) scale_part(0, j);
+      for (int j = 0; j < 4; ++j) scale_part(0, j, gp);
     }
     if (nk > 2) {
-      StageCopy c1 = stage_copy(1);
+      StageCopy c1 = stage_copy(1, sp);
 #pragma unroll
       for (int j = 0; j < kDmaHalf; ++j) {
         copy_a(c1);
@@ -654,9 +660,32 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   if (ACCUM && up.dynamic) up.dynamic = 2;   // blocked order (describe)
   int tile = blockIdx.x;   // unit index (a tile, or half of one: describe_unit)
   if (tile >= up.nunits) return;
-  TileDesc cur = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
-  setup(cur);
-  tile_prologue(cur.nk);
+  // Dynamic order (wgrad with a tile counter): the next tile must be known
+  // before the current tile's last two stages, which carry its first copies.
+  // Thread 0 takes the successor of the next tile from the counter at the
+  // end of the current tile's contraction (and the first successor here);
+  // the index reaches every wave through LDS at the next tile's start.  The
+  // counters start past the workgroups' first tiles (their own indices,
+  // queue_init_kernel); an index past the last tile ends the loop, so every
+  // workgroup stops after finitely many tiles.  Global (not generic)
+  // atomics: a generic one would also count on the LDS counter the loop
+  // waits on.  With a grid that is a multiple of 8 there is one counter per
+  // XCD (workgroup b runs on XCD b % 8): XCD x takes list positions x, x + 8,
+  // ..., so the workgroups sharing its L2 work on neighbouring tiles of the
+  // same experts (one global counter scattered them over the XCDs and raised
+  // the fetched bytes by half).
+  int fetched = 0;
+  if (KGROUPED && up.dynamic && tid == 0)
+    fetched = __hip_atomic_fetch_add(
+        (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int cur_nk;   // contraction steps of the current tile
+  {
+    const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
+    setup(d);
+    tile_prologue(d.nk, 0, 0);
+    cur_nk = d.nk;
+  }
   // A tile's first wait leaves 63 vector-memory operations outstanding.  It
   // sees stages 0 and 1 land when at least 63 operations were issued after
   // them (the previous tile's stores: the counter completes in issue order),
@@ -668,26 +697,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   for (;;) {
-    const int nk = cur.nk;
+    const int nk = cur_nk;
     const int ns = nk >> 1;   // stages
-    // Dynamic order (wgrad with a tile counter): thread 0 takes the index of
-    // this workgroup's next tile now; the value is first needed after the K
-    // loop, where every copy has landed, so waiting for it costs nothing.
-    // The counters start past the workgroups' first tiles (their own
-    // indices, queue_init_kernel); an index past the last tile ends the loop,
-    // so every workgroup stops after finitely many tiles.  A global (not
-    // generic) atomic: a generic one would also count on the LDS counter the
-    // loop waits on.
-    // With a grid that is a multiple of 8 there is one counter per XCD
-    // (workgroup b runs on XCD b % 8): XCD x takes list positions x, x + 8,
-    // ..., so the workgroups sharing its L2 work on neighbouring tiles of the
-    // same experts (one global counter scattered them over the XCDs and
-    // raised the fetched bytes by half).
-    int fetched = 0;
-    if (KGROUPED && up.dynamic && tid == 0)
-      fetched = __hip_atomic_fetch_add(
-          (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
-          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // dynamic order: thread 0 hands on the index it took at the end of the
+    // previous tile's contraction (at least 63 store operations, or a full
+    // wait, lie between: the atomic has completed, and the value costs no
+    // wait); the barrier after the tile's first wait (or, in a tile without
+    // contraction steps, the one below) publishes it
+    if (KGROUPED && up.dynamic && tid == 0) next_lds = fetched;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -739,10 +756,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // of stage st + 2 and the scale group that starts there.  Every copy of
     // stage st + 2 has at least the whole even step 2 st + 2 to land before
     // the wait of odd step 2 st + 3.
-#define MX_EVEN(ST, FULL, CP)                                                               \
+#define MX_EVEN(ST, PF, CP)                                                                 \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
-    const bool pf_ = (FULL) || st_ + 2 < ns;                                                \
+    const bool pf_ = (PF);                                                                  \
     const StepRead rd_ = step_read(2 * st_ + 1);                                            \
     MX_FENCE                                                                                \
     MX_MFMA(0, 0, 0) load_a(rd_, 1, 0); MX_FENCE                                            \
@@ -756,7 +773,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     MX_MFMA(2, 0, 0)                                                                        \
     if (pf_) {                                                                              \
       __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): this wave's reads of stage st */  \
-      __syncthreads();                    /* slot st % 2 is free */                         \
+      __syncthreads();                    /* stage st's slot is free */                     \
     }                                                                                       \
     MX_FENCE                                                                                \
     MX_MFMA(2, 1, 0) if (pf_) copy_a(CP); MX_FENCE                                          \
@@ -767,13 +784,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     MX_MFMA(3, 2, 0) MX_FENCE                                                               \
     MX_MFMA(3, 3, 0) if (pf_) copy_a(CP); if (pf_) copy_b(CP); MX_FENCE                     \
   }
-#define MX_ODD(ST, FULL, CP)                                                                \
+#define MX_ODD(ST, NX, PF, SG, G, GP, CP)                                                   \
   {                                                                                         \
     const int st_ = (ST);                                                                   \
-    const bool nx_ = (FULL) || st_ + 1 < ns;                                                \
-    const bool pf_ = (FULL) || st_ + 2 < ns;                                                \
-    const bool sg_ = pf_ && (((st_ + 2) * 2) % kScaleSteps == 0);                           \
-    const int g_ = ((st_ + 2) * 2) / kScaleSteps;                                           \
+    const bool nx_ = (NX);                                                                  \
+    const bool pf_ = (PF);                                                                  \
+    const bool sg_ = (SG);                                                                  \
+    const int g_ = (G);                                                                     \
     if (nx_) {                                                                              \
       /* stage st + 1 landed; only the 6 copies of stage st + 2 may be pending */          \
       if (pf_) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));                                    \
@@ -795,48 +812,78 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     MX_MFMA(2, 2, 1) if (nx_) load_b(rd_, 0, 2); if (pf_) copy_b(CP); MX_FENCE              \
     MX_MFMA(2, 3, 1) MX_FENCE                                                               \
     MX_MFMA(3, 0, 1) if (nx_) load_a(rd_, 0, 3); if (pf_) copy_a(CP);                       \
-    if (sg_) scale_part(g_, 0); MX_FENCE                                                    \
-    MX_MFMA(3, 1, 1) if (pf_) copy_b(CP); if (sg_) scale_part(g_, 1); MX_FENCE              \
-    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (sg_) scale_part(g_, 2); MX_FENCE       \
-    MX_MFMA(3, 3, 1) if (sg_) scale_part(g_, 3); MX_FENCE                                   \
+    if (sg_) scale_part(g_, 0, GP); MX_FENCE                                                \
+    MX_MFMA(3, 1, 1) if (pf_) copy_b(CP); if (sg_) scale_part(g_, 1, GP); MX_FENCE          \
+    MX_MFMA(3, 2, 1) if (nx_) load_b(rd_, 0, 3); if (sg_) scale_part(g_, 2, GP); MX_FENCE   \
+    MX_MFMA(3, 3, 1) if (sg_) scale_part(g_, 3, GP); MX_FENCE                               \
   }
 
-    // steady state (every stage has a successor two ahead), then the last
-    // two stages with those checks
+    // steady state (every stage has a successor two ahead)
     int st = 0;
     for (; st + 2 < ns; ++st) {
-      StageCopy cp = stage_copy(st + 2);
+      StageCopy cp = stage_copy(st + 2, spar);
       MX_EVEN(st, true, cp)
-      MX_ODD(st, true, cp)
+      MX_ODD(st, true, true, ((st + 2) * 2) % kScaleSteps == 0, ((st + 2) * 2) / kScaleSteps,
+             gpar, cp)
     }
+    // The next tile.  Where both tiles have at least two stages, the copy
+    // ring runs on into it: the last two stages of this tile carry the copies
+    // of its stages 0 and 1 (and its scale group 0) in the slots and at the
+    // places of the steady state, so they land under this tile's MFMAs
+    // instead of being issued between the tiles (the set-up between two
+    // tiles took 2-15 % of the tile time, mostly the issue of those copies).
+    // Its stage 0 takes the slot after this tile's last stage, its scale
+    // group 0 the buffer that this tile's last group does not use (free: the
+    // group before that one was last read in the even step of stage ns - 2,
+    // before its barrier).
+    // (Only the next tile's step count is kept through the last stages; the
+    // rest of its description is recomputed where the ring does not run on:
+    // kept, it raised the register pressure enough to spill inside the loop.)
+    int next = tile + (int)gridDim.x;
+    if (KGROUPED && up.dynamic) {
+      if (nk == 0) __syncthreads();   // no first wait and barrier above
+      next = __builtin_amdgcn_readfirstlane(next_lds) * up.nq + (int)(blockIdx.x & (up.nq - 1));
+    }
+    const bool has_next = next < up.nunits;
+    int nk_next = 0;
+    if (has_next) {
+      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+      nk_next = d.nk;
+      // this tile issues no more copies of its own: where the ring runs on,
+      // its copy bases become the next tile's
+      if (ns >= 2 && d.nk >= 4) setup(d);
+    }
+    const bool chain = has_next && ns >= 2 && nk_next >= 4;
+    const int spar_n = (spar + ns) & 1;
+    const int gpar_n = (gpar + (nk > 0 ? (nk - 1) / kScaleSteps : 0) + 1) & 1;
     for (; st < ns; ++st) {
-      StageCopy cp = stage_copy(st + 2);
-      MX_EVEN(st, false, cp)
-      MX_ODD(st, false, cp)
+      StageCopy cp = stage_copy(st + 2 - ns, spar_n);
+      MX_EVEN(st, chain, cp)
+      MX_ODD(st, st + 1 < ns, chain, chain && st + 2 == ns, 0, gpar_n, cp)
     }
 #undef MX_EVEN
 #undef MX_ODD
 #undef MX_FENCE
 #undef MX_MFMA
-
-    // Next tile: once every wave has read the last stage (lgkmcnt(0) + the
-    // barrier), both LDS slots and both scale buffers are free, so its first
-    // stages are copied while this tile's results are stored.
-    int next = tile + (int)gridDim.x;
-    if (KGROUPED && up.dynamic) {
-      if (tid == 0) next_lds = fetched;
+    // dynamic order: the successor of the next tile (see above)
+    if (KGROUPED && up.dynamic && has_next && tid == 0)
+      fetched = __hip_atomic_fetch_add(
+          (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
+          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (has_next && !chain) {
+      // Once every wave has read the last stage (lgkmcnt(0) + the barrier),
+      // both LDS slots and both scale buffers are free: the next tile's first
+      // stages are copied while this tile's results are stored.
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
-      next = __builtin_amdgcn_readfirstlane(next_lds) * up.nq + (int)(blockIdx.x & (up.nq - 1));
-    }
-    TileDesc nxt;
-    nxt.nk = 0;
-    if (next < up.nunits) {
-      nxt = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+      setup(d);
+      tile_prologue(d.nk, spar_n, gpar_n);
+    } else if (SWIGLU) {
+      // the SwiGLU epilogue's LDS scratch: the scale buffer of this tile's
+      // last group, free once every wave has read it
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
-      setup(nxt);
-      tile_prologue(nxt.nk);
     }
 
     // The epilogue's tile bounds and output base are recomputed from the
@@ -1005,12 +1052,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
               sbytes |= xb << (8 * i);
             }
             if (p.q_row != nullptr) {
-              // row-wise through this wave's 2 KiB of the second scale buffer
-              // (free until the next tile's K loop loads scale group 1): the
+              // row-wise through this wave's 2 KiB of the scale buffer that
+              // the next tile's scale group 0 does not use (free until its K
+              // loop loads group 1 there): the
               // 32 x 32 block row-major, then lane l reads half l % 2 of row
               // l / 2 (16 values of one row: one scale, 16 codes, one store)
               uint16_t* xw = reinterpret_cast<uint16_t*>(
-                  smem + kSlots * kStageBytes + kScaleBuf + 2048 * wave);
+                  smem + kSlots * kStageBytes + ((gpar_n + 1) & 1) * kScaleBuf + 2048 * wave);
 #pragma unroll
               for (int r = 0; r < 16; ++r)
                 xw[(8 * (r / 4) + 4 * half + (r % 4)) * 32 + c] = (uint16_t)a[r];
@@ -1103,14 +1151,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         }
       }
     }
-    if (next >= up.nunits) break;
+    if (!has_next) break;
     // the store loops above issue one operation per register (256 per wave
     // for every row inside the tile) or, accumulating, 64 loads and 64
     // stores
     if (!(KGROUPED ? (!ACCUM || nk > 0) : (ed.row_lo == 0 && ed.row_hi == BM)))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     tile = next;
-    cur = nxt;
+    cur_nk = nk_next;
+    spar = spar_n;
+    gpar = gpar_n;
   }
 }
 

@@ -492,7 +492,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ ExpertTable table;
   __shared__ int32_t next_lds;          // dynamic order: a tile index, from thread 0
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t esz = OUT_BF16 ? 2 : 4;
@@ -506,17 +505,35 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   // chunk position i%8, which holds the row's chunk (i%8) ^ (i/8).  The scale
   // groups use 16 rows x 16 bytes per instruction: lane i -> row 16 j + i/4,
   // bytes 4 (i%4) .. 4 (i%4) + 3 of the row's group.
-  const int cr = lane >> 3;
-  const int cchunk = (lane & 7) ^ cr;
-  const int fr = lane & 31;   // operand row within a 32-row fragment
-  const int fg = lane >> 5;   // contraction half of the lane
-
-  // Per-lane copy offsets (launch constants): row i/8 of an 8-row part and
-  // its swizzled chunk; rows of the part and of the wave go into the scalar
-  // base.  A wave whose 64 rows would lie past the operand (T < 256) copies
-  // rows of the first waves instead; their results are not stored.
-  const uint32_t ca = (uint32_t)(cr * p.lda + cchunk * 16);
-  const uint32_t cb = (uint32_t)(cr * p.ldb + cchunk * 16);
+  // Per-lane copy offsets: row i/8 of an 8-row part and its swizzled chunk;
+  // rows of the part and of the wave go into the scalar base.  A wave whose
+  // 64 rows would lie past the operand (T < 256) copies rows of the first
+  // waves instead; their results are not stored.
+  // Per-lane LDS offsets of this wave's fragments: row wm WT + fr (A) or
+  // wn WT + fr (B), fr = lane % 32, g = lane / 32; for step half h the lane's
+  // chunks are 4 h + g and 4 h + 2 + g, at positions p0 ^ 4h and p0 ^ 4h ^ 2
+  // with p0 = g ^ (fr & 7) (fragment rows 32 i + fr share fr & 7); fragment
+  // i adds 32 rows.
+  // All of them are formed from the hardware lane id at every tile start
+  // (volatile: not kept through the epilogue, where the accumulating wgrad
+  // had no register left for them and spilled one; the reload's wait then
+  // drained every copy once per stage).
+  uint32_t ca, cb, rA, rB, rX, rH, rSA, rSB;
+  auto lane_consts = [&]() {
+    uint32_t ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int cr = (int)(ln >> 3), cchunk = (int)(ln & 7) ^ cr;
+    ca = (uint32_t)(cr * p.lda + cchunk * 16);
+    cb = (uint32_t)(cr * p.ldb + cchunk * 16);
+    const int fr = (int)(ln & 31), fg = (int)(ln >> 5);
+    const int p0 = fg ^ (fr & 7);
+    rA = (uint32_t)((wm * WT + fr) * BK + p0 * 16);
+    rB = (uint32_t)(kOffB + (wn * WT + fr) * BK + p0 * 16);
+    rX = (uint32_t)(((p0 ^ 2) - p0) * 16);   // +-32: chunk 2 + g
+    rH = (uint32_t)(((p0 ^ 4) - p0) * 16);   // +-64: second half of the stage
+    rSA = (uint32_t)((wm * WT + fr) * kScaleRow + fg);
+    rSB = (uint32_t)(kScOffB + (wn * WT + fr) * kScaleRow + fg);
+  };
   const uint8_t *a_base, *b_base, *sa_base, *sb_base;
   int s_nblk;
   // LDS slot and scale-buffer parity of the current tile's stage 0 and scale
@@ -593,17 +610,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   // the other set is filled for step kt + 1
   v8i af[2][4], bf[2][4];
   int as[2][4], bs[2][4];
-  // Per-lane LDS offsets of this wave's fragments: row wm WT + fr (A) or
-  // wn WT + fr (B); for step half h the lane's chunks are 4 h + g and
-  // 4 h + 2 + g, at positions p0 ^ 4h and p0 ^ 4h ^ 2 with p0 = g ^ (fr & 7)
-  // (fragment rows 32 i + fr share fr & 7); fragment i adds 32 rows.
-  const int p0 = fg ^ (fr & 7);
-  const uint32_t rA = (uint32_t)((wm * WT + fr) * BK + p0 * 16);
-  const uint32_t rB = (uint32_t)(kOffB + (wn * WT + fr) * BK + p0 * 16);
-  const uint32_t rX = (uint32_t)(((p0 ^ 2) - p0) * 16);   // +-32: chunk 2 + g
-  const uint32_t rH = (uint32_t)(((p0 ^ 4) - p0) * 16);   // +-64: second half of the stage
-  const uint32_t rSA = (uint32_t)((wm * WT + fr) * kScaleRow + fg);
-  const uint32_t rSB = (uint32_t)(kScOffB + (wn * WT + fr) * kScaleRow + fg);
   // this lane's LDS addresses of fragment 0 of MFMA step kt (A chunk g, A
   // chunk 2 + g, B chunk g, B chunk 2 + g, A scale, B scale)
   struct StepRead {
@@ -680,6 +686,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int cur_nk;   // contraction steps of the current tile
+  lane_consts();
   {
     const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
     setup(d);
@@ -698,13 +705,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 
   for (;;) {
     const int nk = cur_nk;
+    lane_consts();
     const int ns = nk >> 1;   // stages
-    // dynamic order: thread 0 hands on the index it took at the end of the
-    // previous tile's contraction (at least 63 store operations, or a full
-    // wait, lie between: the atomic has completed, and the value costs no
-    // wait); the barrier after the tile's first wait (or, in a tile without
-    // contraction steps, the one below) publishes it
-    if (KGROUPED && up.dynamic && tid == 0) next_lds = fetched;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -715,6 +717,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     if (nk > 0) {
       // stages 0 and 1 landed (the wait before the tile loop explains 63)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(63));
+      // dynamic order: thread 0 hands on the index it took at the end of the
+      // previous tile's contraction; the previous tile's epilogue memory
+      // operations (at least 64) or a full wait lie between, so this wait
+      // covers the atomic too, and the barrier publishes the value
+      if (KGROUPED && up.dynamic && tid == 0) next_lds = fetched;
       __syncthreads();
       // step 0 through an opaque index: with constant offsets its addresses
       // would be precomputed once and spilled, and the reload's wait counts
@@ -841,7 +848,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // kept, it raised the register pressure enough to spill inside the loop.)
     int next = tile + (int)gridDim.x;
     if (KGROUPED && up.dynamic) {
-      if (nk == 0) __syncthreads();   // no first wait and barrier above
+      if (nk == 0) {   // no first wait and barrier above
+        if (tid == 0) next_lds = fetched;
+        __syncthreads();
+      }
       next = __builtin_amdgcn_readfirstlane(next_lds) * up.nq + (int)(blockIdx.x & (up.nq - 1));
     }
     const bool has_next = next < up.nunits;

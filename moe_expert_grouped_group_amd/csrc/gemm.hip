@@ -307,16 +307,20 @@ struct TileDesc {
   int32_t split;       // one contraction half of a split tile: add into C atomically
   int64_t m0c;         // M-grouped: first copied row (token) of the tile
   int32_t nt;          // M-grouped: column tile index
+  int32_t g;           // M-grouped: the tile's expert
 };
 
 template <bool KGROUPED, bool SWIGLU = false>
 __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTable* t, int tile,
-                                             int64_t esz, int dynamic = 0) {
+                                             int64_t esz, int dynamic = 0, int g_lo = 0,
+                                             int g_hi = -1) {
   TileDesc d;
   if (!KGROUPED) {
     const int mt = tile / p.ntiles_n, nt = tile % p.ntiles_n;
-    // expert g: the last with tpre[g] <= mt (binary search over G + 1 entries)
-    int lo = 0, hi = p.G;                    // tpre[lo] <= mt < tpre[hi]
+    // expert g: the last with tpre[g] <= mt (binary search over G + 1
+    // entries, or over [g_lo, g_hi) where the caller knows that the expert
+    // lies there: the tiles of a workgroup come in increasing order)
+    int lo = g_lo, hi = g_hi < 0 ? p.G : g_hi;   // tpre[lo] <= mt < tpre[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (t->tpre[mid] <= mt) lo = mid; else hi = mid;
@@ -344,6 +348,7 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.c = reinterpret_cast<char*>(p.c) + (m0c * p.ldc + n0) * esz;
     d.m0c = m0c;
     d.nt = nt;
+    d.g = g;
   } else {
     // The list of tiles (experts in decreasing order of tokens) is consumed
     // from both ends at once: of the two workgroups of a pair (tiles 2q and
@@ -396,6 +401,7 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     d.nk = (int32_t)(len / KSTEP);
     d.nblk = (int32_t)(len / 32);
     d.c = reinterpret_cast<char*>(p.c) + (g * p.c_gstride + m0 * p.ldc + n0) * esz;
+    d.g = 0;
   }
   // every lane computed the same values: keep them in scalar registers
   d.a = uniform_ptr(d.a);
@@ -460,15 +466,16 @@ __device__ __forceinline__ UnitPlan plan_units(const GemmArgs& p, const ExpertTa
 
 template <bool KGROUPED, bool SWIGLU = false>
 __device__ __forceinline__ TileDesc describe_unit(const GemmArgs& p, const ExpertTable* t,
-                                                  const UnitPlan& up, int unit, int64_t esz) {
+                                                  const UnitPlan& up, int unit, int64_t esz,
+                                                  int g_lo = 0, int g_hi = -1) {
   if (KGROUPED || SWIGLU || unit < up.first_split) {
-    TileDesc d = describe<KGROUPED, SWIGLU>(p, t, unit, esz, up.dynamic);
+    TileDesc d = describe<KGROUPED, SWIGLU>(p, t, unit, esz, up.dynamic, g_lo, g_hi);
     d.split = 0;
     return d;
   }
   const int v = unit - up.first_split;
   const int half = v & 1;
-  TileDesc d = describe<KGROUPED>(p, t, up.first_split + (v >> 1), esz);
+  TileDesc d = describe<KGROUPED>(p, t, up.first_split + (v >> 1), esz, 0, g_lo, g_hi);
   // contraction bytes [half kc/2, (half + 1) kc/2) of the tile (kc % 1024 == 0:
   // each half is a whole number of stages and of 8-step scale groups)
   const int64_t hk = half * (p.kc / 2);
@@ -686,12 +693,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         (__attribute__((address_space(1))) int32_t*)p.queue + (blockIdx.x & (up.nq - 1)), 1,
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int cur_nk;   // contraction steps of the current tile
+  int cur_g = 0;   // M-grouped: its expert (the next tile's lies at or after it)
   lane_consts();
   {
     const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
     setup(d);
     tile_prologue(d.nk, 0, 0);
     cur_nk = d.nk;
+    cur_g = d.g;
   }
   // A tile's first wait leaves 63 vector-memory operations outstanding.  It
   // sees stages 0 and 1 land when at least 63 operations were issued after
@@ -855,10 +864,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       next = __builtin_amdgcn_readfirstlane(next_lds) * up.nq + (int)(blockIdx.x & (up.nq - 1));
     }
     const bool has_next = next < up.nunits;
-    int nk_next = 0;
+    int nk_next = 0, g_next = 0;
     if (has_next) {
-      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz, cur_g);
       nk_next = d.nk;
+      g_next = d.g;
       // this tile issues no more copies of its own: where the ring runs on,
       // its copy bases become the next tile's
       if (ns >= 2 && d.nk >= 4) setup(d);
@@ -886,7 +896,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       // stages are copied while this tile's results are stored.
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       __syncthreads();
-      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz);
+      const TileDesc d = describe_unit<KGROUPED, SWIGLU>(p, &table, up, next, esz, g_next,
+                                                         g_next + 1);
       setup(d);
       tile_prologue(d.nk, spar_n, gpar_n);
     } else if (SWIGLU) {
@@ -900,7 +911,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
     // expert table (LDS) rather than kept from the tile start: held across
     // the K loop they are spilled, and the reload's wait on the vector memory
     // counter would also wait for the next tile's copies issued above.
-    const TileDesc ed = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz);
+    const TileDesc ed = describe_unit<KGROUPED, SWIGLU>(p, &table, up, tile, esz, cur_g,
+                                                        cur_g + 1);
 
     // ---- epilogue: accumulator r of acc[i][j] in lane l is C[m][n] with
     // m = wm WT + 32 i + 8 (r/4) + 4 (l/32) + r%4 and n = wn WT + 32 j + l%32.
@@ -1169,6 +1181,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     tile = next;
     cur_nk = nk_next;
+    cur_g = g_next;
     spar = spar_n;
     gpar = gpar_n;
   }

@@ -399,8 +399,8 @@ def bench_fused_mlp(steps, warmup):
     dyc = dyo
     da = torch.empty(t, f, dtype=bf, device="cuda")
     dw2 = torch.empty(g, k, f, dtype=bf, device="cuda")
-    dh = torch.empty(t, n2, dtype=bf, device="cuda")
-    dho, db1 = mx.group_quantize_requant(dh.zero_(), ms, with_dbias=True)
+    dho, db1 = mx.group_quantize_requant(torch.zeros(t, n2, dtype=bf, device="cuda"), ms,
+                                         with_dbias=True)
     dhc = dho
     dx = torch.empty(t, k, dtype=bf, device="cuda")
     dw1 = torch.empty(g, n2, k, dtype=bf, device="cuda")
@@ -422,9 +422,10 @@ def bench_fused_mlp(steps, warmup):
                                    w2o.col_scale, ms, t, k, f, bf, da)),
         ("fc2_wgrad", lambda: gemm("TN", dyc.col_data, dyc.col_scale, ao.col_data, ao.col_scale,
                                    ms, t, k, f, bf, dw2, workspace=gws)),
-        ("swiglu_bwd", lambda: mx.swiglu_bwd(h, da, out=dh)),
-        ("quant_requant_dh_dbias", lambda: mx.group_quantize_requant(
-            dh, ms, with_dbias=True, out=dho, dbias=db1, workspace=ws)),
+        # the SwiGLU backward fused with the quantize + requantize (+ dbias)
+        # of dh for the FC1 backward: dh itself is never written
+        ("swiglu_bwd_quant_dbias", lambda: mx.swiglu_bwd_quantize(
+            h, da, ms, with_dbias=True, out=dho, dbias=db1, workspace=ws)),
         ("fc1_dgrad", lambda: gemm("NN", dho.row_data, dho.row_scale, w1o.col_data,
                                    w1o.col_scale, ms, t, n2, k, bf, dx)),
         ("fc1_wgrad", lambda: gemm("TN", dhc.col_data, dhc.col_scale, xc.col_data, xc.col_scale,
@@ -479,6 +480,45 @@ def bench_fc1_swiglu(steps, warmup):
             "fused_ms": round(fused_ms, 4),
             "note": "same h and MXFP8 bytes either way (tests); the fused MLP step uses the "
                     "fused launch"}
+
+
+def bench_swiglu_bwd_quant(steps, warmup):
+    """The fused MLP's SwiGLU backward (83968 tokens, F = 1024, 64 experts)
+    fused with the row-wise quantize, column-wise requantize and dbias of its
+    output dh, against the two launches it replaces (swiglu_bwd, then
+    group_quantize_requant of dh with dbias)."""
+    import torch
+
+    import moe_expert_grouped_group_amd as mx
+    from moe_expert_grouped_group_amd import workloads as wl
+
+    del warmup
+    name = "nemotron_proxy_mlp"
+    splits = wl.splits_for(name)
+    t, f = int(splits.sum()), wl.make(name, parts=set()).ffn // 2
+    ms = torch.from_numpy(splits).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+    h = (torch.randn(t, 2 * f, device="cuda", generator=gen) * 3).to(bf)
+    da = torch.randn(t, f, device="cuda", generator=gen).to(bf)
+    dh = torch.empty_like(h)
+    out, db = mx.group_quantize_requant(dh.zero_(), ms, with_dbias=True)
+    ws = torch.empty(mx.dbias_workspace_bytes(t, 2 * f), dtype=torch.uint8, device="cuda")
+    bwd = lambda: mx.swiglu_bwd(h, da, out=dh)  # noqa: E731
+    qr = lambda: mx.group_quantize_requant(dh, ms, with_dbias=True, out=out,  # noqa: E731
+                                           dbias=db, workspace=ws)
+    fused = lambda: mx.swiglu_bwd_quantize(h, da, ms, with_dbias=True, out=out,  # noqa: E731
+                                           dbias=db, workspace=ws)
+    bwd_ms = _time_outside(bwd, steps)
+    qr_ms = _time_outside(qr, steps)
+    fused_ms = _time_outside(fused, steps)
+    nbytes = t * 2 * f * 2 + t * f * 2 + 2 * t * 2 * f * (1 + 1 / 32)
+    return {"tokens": t, "ffn": f, "swiglu_bwd_ms": round(bwd_ms, 4),
+            "quant_requant_dbias_ms": round(qr_ms, 4), "unfused_ms": round(bwd_ms + qr_ms, 4),
+            "fused_ms": round(fused_ms, 4),
+            "fused_gbs": round(nbytes / (fused_ms * 1e-3) / 1e9, 1),
+            "note": "same MXFP8 bytes and dbias bits either way (tests); the fused MLP step uses "
+                    "the fused launch; fused_gbs counts h and da read, both MXFP8 copies written"}
 
 
 def bench_group_quantize(steps, warmup):
@@ -823,6 +863,7 @@ def summarize_main(argv):
 
 OTHERS.update({"skewed_dsv3": bench_skewed_linear, "nemotron_proxy_mlp": bench_fused_mlp,
                "fc1_swiglu_quantize": bench_fc1_swiglu,
+               "swiglu_bwd_quantize": bench_swiglu_bwd_quant,
                "group_quantize_131072x7168": bench_group_quantize})
 
 

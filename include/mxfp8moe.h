@@ -417,6 +417,31 @@ mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, 
                               uint16_t* dh, void* stream);
 
 /*
+ * mxfp8_swiglu_bwd_quantize -- the SwiGLU backward fused with the quantize of
+ * its output for the FC1 backward of the fused expert MLP ([P3545]
+ * Description: FC1 -> activation -> FC2 as one op; the FC1 dgrad reads the
+ * row-wise and its wgrad the column-wise copy of dh, and [P3244] Description
+ * and Greptile flowchart: the column-wise copy requantized from the
+ * dequantized row-wise values, the bias gradient reduced from them).  dh =
+ * mxfp8_swiglu_bwd(h, da) is formed in registers and handled exactly as
+ * mxfp8_group_quantize_requant handles a [T, 2F] tensor, without writing dh:
+ * every output byte, and dbias bit for bit, equals mxfp8_swiglu_bwd followed
+ * by mxfp8_group_quantize_requant.
+ *   h      [T, 2F] bf16 (gate | up, device);  da [T, F] bf16 (device)
+ *   q_row  [T, 2F] u8,  s_row [T, 2F/32] u8
+ *   q_col  [2F, T] u8,  s_col [2F, T/32] u8
+ *   m_splits, G, dbias [G, 2F] fp32, workspace: as mxfp8_group_quantize_requant
+ *   with K = 2F (dbias optional: NULL skips it and needs no workspace).
+ * Errors: EINVAL for NULL pointers (T > 0), T % 128, F % 256, and as
+ * mxfp8_requant_colwise for dbias.
+ */
+mxfp8_status mxfp8_swiglu_bwd_quantize(const uint16_t* h, const uint16_t* da, int64_t T,
+                                       int64_t F, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                       uint8_t* s_col, const int64_t* m_splits, int32_t G,
+                                       float* dbias, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * mxfp8_convert_sweep -- diagnostic: runs the device's E4M3 / E8M0 conversion
  * helpers (the ones every quantize kernel encodes and decodes with) over
  * every (value, scale byte) pair, so that a test can compare them with an

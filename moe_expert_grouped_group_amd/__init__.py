@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     convert_sweep, dbias_workspace_bytes, group_quantize, group_quantize_requant,
     group_quantize_requant_noalloc, grouped_dbias, grouped_gemm, grouped_gemm_swiglu_quantize,
     grouped_gemm_wgrad_accumulate,
-    grouped_scaled_bias_grad, gemm_workspace_bytes, requant_colwise, swiglu_bwd, swiglu_fwd,
+    grouped_scaled_bias_grad, gemm_workspace_bytes, requant_colwise, swiglu_bwd,
+    swiglu_bwd_quantize, swiglu_fwd,
     swiglu_quantize, validate_splits)
 from ._native import load as load_library, lib_path  # noqa: F401

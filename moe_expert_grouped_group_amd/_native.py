@@ -49,6 +49,8 @@ SIGNATURES = {
                                                        c_i64, c_vp, c_i32, c_vp, c_size, c_vp]),
     "mxfp8_swiglu_fwd": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "mxfp8_swiglu_bwd": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "mxfp8_swiglu_bwd_quantize": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_i32, c_vp, c_vp, c_size, c_vp]),
     "mxfp8_swiglu_quantize": (c_i32, [c_vp, c_i64, c_i64, c_u32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "mxfp8_scaled_bias_workspace_bytes": (c_size, [c_i64, c_i64]),
     "mxfp8_grouped_scaled_bias_grad": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp,

@@ -435,6 +435,36 @@ def swiglu_fwd(h, out=None, stream=None):
     return out
 
 
+def swiglu_bwd_quantize(h, da, m_splits=None, with_dbias=False, out=None, dbias=None,
+                        workspace=None, stream=None):
+    """SwiGLU backward of h [T, 2F] and da [T, F] (bf16) quantized as
+    group_quantize_requant quantizes dh [T, 2F], without writing dh: the bytes
+    (and dbias [G, 2F]) of swiglu_bwd followed by group_quantize_requant.
+    Returns the tensor, or (tensor, dbias) with_dbias."""
+    lib = _lib()
+    t, k = h.shape
+    f = k // 2
+    _need(h, torch.bfloat16, (t, 2 * f), "h")
+    _need(da, torch.bfloat16, (t, f), "da")
+    out = _mx_outputs(out, ROWWISE | COLWISE, t, k, h)
+    g = 0
+    ms = None
+    if with_dbias:
+        ms = _splits(m_splits)
+        g = ms.numel()
+        if dbias is None:
+            dbias = _empty((g, k), torch.float32, h)
+        _need(dbias, torch.float32, (g, k), "dbias")
+        workspace = _workspace(t, k, h, workspace)
+    st = lib.mxfp8_swiglu_bwd_quantize(
+        _ptr(h), _ptr(da), t, f, _ptr(out.row_data), _ptr(out.row_scale), _ptr(out.col_data),
+        _ptr(out.col_scale), _ptr(ms), g, _ptr(dbias) if with_dbias else None,
+        _ptr(workspace) if with_dbias else None,
+        workspace.numel() * workspace.element_size() if with_dbias else 0, _stream(stream))
+    _native.check(st, "mxfp8_swiglu_bwd_quantize")
+    return (out, dbias) if with_dbias else out
+
+
 def swiglu_bwd(h, da, out=None, stream=None):
     """Gradient of swiglu_fwd w.r.t. h, given da [T, F]; returns bf16 [T, 2F]."""
     lib = _lib()

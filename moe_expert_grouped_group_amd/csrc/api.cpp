@@ -422,6 +422,35 @@ mxfp8_status mxfp8_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, 
   return hip_status(mx::launch_swiglu_bwd(h, da, T, F, dh, as_stream(stream)), fn);
 }
 
+mxfp8_status mxfp8_swiglu_bwd_quantize(const uint16_t* h, const uint16_t* da, int64_t T,
+                                       int64_t F, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                                       uint8_t* s_col, const int64_t* m_splits, int32_t G,
+                                       float* dbias, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const char* fn = "mxfp8_swiglu_bwd_quantize";
+  REQUIRE(T == 0 || (h && da && q_row && s_row && q_col && s_col), "%s: NULL pointer", fn);
+  REQUIRE(T >= 0 && T % 128 == 0, "%s: T = %lld must be a multiple of 128", fn, (long long)T);
+  REQUIRE(F > 0 && F % 256 == 0, "%s: F = %lld must be a positive multiple of 256", fn,
+          (long long)F);
+  const int64_t K = 2 * F;
+  float* partial = nullptr;
+  if (dbias != nullptr) {
+    mxfp8_status st = check_device_splits(m_splits, G, fn);
+    if (st != MXFP8_OK) return st;
+    REQUIRE((workspace != nullptr || T == 0) &&
+                workspace_bytes >= mxfp8_dbias_workspace_bytes(T, K),
+            "%s: dbias needs a workspace of %zu bytes", fn, mxfp8_dbias_workspace_bytes(T, K));
+    partial = static_cast<float*>(workspace);
+  }
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0)
+    e = mx::launch_swiglu_bwd_quant(h, da, T, F, q_row, s_row, q_col, s_col, partial, st);
+  if (e == hipSuccess && dbias != nullptr)
+    e = mx::launch_dbias_finalize(partial, m_splits, G, T, K, dbias, st);
+  return hip_status(e, fn);
+}
+
 size_t mxfp8_convert_sweep_bytes(int32_t mode) { return mx::convert_sweep_bytes(mode); }
 
 mxfp8_status mxfp8_convert_sweep(int32_t mode, void* out, size_t out_bytes, void* stream) {

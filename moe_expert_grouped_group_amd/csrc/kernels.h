@@ -38,6 +38,9 @@ hipError_t launch_swiglu_quant(const uint16_t* h, int64_t T, int64_t F, uint8_t*
                                uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st);
 hipError_t launch_swiglu_bwd(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
                              uint16_t* dh, hipStream_t st);
+hipError_t launch_swiglu_bwd_quant(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
+                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                   float* partial, hipStream_t st);
 size_t convert_sweep_bytes(int32_t mode);   // 0 for an unknown mode
 // The file-scope device scratch of quantize.hip: its size, and its address on
 // the current device (looked up once per device).

@@ -549,10 +549,18 @@ __global__ __launch_bounds__(256) void dscale_finalize_kernel(const float* __res
 
 // dbias[g, k] = sum over the 128-row tiles of expert g of partial[tile, k],
 // in tile order.  grid = (G, ceil(K / 256)).
+// dbias[g, k] = the sum of the expert's tile partials of column k.  A block
+// takes 64 columns of one expert; the four waves each sum every fourth tile
+// of the expert in tile order, and the four sums are added in wave order: a
+// fixed order, so dbias does not depend on timing, with four times the loads
+// in flight of one summing thread per column (the Nemotron-proxy dh, whose
+// largest expert has 172 tiles, finalized in 65 us with one thread per
+// column).
 __global__ __launch_bounds__(256) void dbias_finalize_kernel(
     const float* __restrict__ partial, const int64_t* __restrict__ m_splits, int32_t G, int64_t T,
     int64_t K, float* __restrict__ dbias) {
   __shared__ int64_t red[256];
+  __shared__ float part[4][64];
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t acc = 0;
@@ -565,14 +573,20 @@ __global__ __launch_bounds__(256) void dbias_finalize_kernel(
   }
   const int64_t off = red[0];
   const int64_t mg = max(m_splits[g], (int64_t)0);
-  const int64_t k = (int64_t)blockIdx.y * 256 + tid;
-  if (k >= K) return;
+  const int w = tid >> 6, c = tid & 63;
+  const int64_t k = (int64_t)blockIdx.y * 64 + c;
   // tiles of the expert, clipped to the token count (splits that break the
   // contract must not make the kernel read out of bounds)
   const int64_t first = min(off, T) / kTileT, last = min(off + mg, T) / kTileT;
   float s = 0.f;
-  for (int64_t tile = first; tile < last; ++tile) s += partial[tile * K + k];
-  dbias[(int64_t)g * K + k] = s;
+  if (k < K) {
+#pragma unroll 4
+    for (int64_t tile = first + w; tile < last; tile += 4) s += partial[tile * K + k];
+  }
+  part[w][c] = s;
+  __syncthreads();
+  if (w == 0 && k < K)
+    dbias[(int64_t)g * K + k] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
 }
 
 // ---------------------------------------------------------------------------
@@ -624,6 +638,32 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint32_t* __restr
   }
 }
 
+// SwiGLU backward of one bf16 pair of each of gate, up and da (the same
+// arithmetic for swiglu_bwd_kernel and swiglu_bwd_quant_kernel, so that the
+// fused kernel's dh equals the written one bit for bit): d gate = da * up * s
+// * (1 + gate (1 - s)) and d up = da * gate * s with s = sigmoid(gate), in
+// fp32, rounded to bf16 (nearest even).  s from the hardware base-2
+// exponential and reciprocal, as silu_f forms it (a few ulp of fp32, far
+// inside the half bf16 ulp of the rounding; the library exp and an IEEE
+// division cost the fused kernel about a third of its time); for gate below
+// about -88 the exponential overflows and s is 0, as with the library form.
+__device__ __forceinline__ void swiglu_bwd_pair(uint32_t gw, uint32_t uw, uint32_t dw,
+                                                uint32_t& og, uint32_t& ou) {
+  og = 0;
+  ou = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float g = bf16_to_f32((gw >> (16 * j)) & 0xFFFFu);
+    const float u = bf16_to_f32((uw >> (16 * j)) & 0xFFFFu);
+    const float d = bf16_to_f32((dw >> (16 * j)) & 0xFFFFu);
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+    const float dg = d * u * s * (1.0f + g * (1.0f - s));
+    const float du = d * g * s;
+    og |= f32_to_bf16(dg) << (16 * j);
+    ou |= f32_to_bf16(du) << (16 * j);
+  }
+}
+
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint32_t* __restrict__ h,
                                                          const uint32_t* __restrict__ da,
                                                          int64_t T, int64_t F,
@@ -633,21 +673,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint32_t* __restr
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * 256) {
     const int64_t row = i / f2, c = i % f2;
-    const uint32_t gw = h[row * F + c];
-    const uint32_t uw = h[row * F + f2 + c];
-    const uint32_t dw = da[i];
-    uint32_t og = 0, ou = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float g = bf16_to_f32((gw >> (16 * j)) & 0xFFFFu);
-      const float u = bf16_to_f32((uw >> (16 * j)) & 0xFFFFu);
-      const float d = bf16_to_f32((dw >> (16 * j)) & 0xFFFFu);
-      const float s = 1.0f / (1.0f + expf(-g));
-      const float dg = d * u * s * (1.0f + g * (1.0f - s));
-      const float du = d * g * s;
-      og |= f32_to_bf16(dg) << (16 * j);
-      ou |= f32_to_bf16(du) << (16 * j);
-    }
+    uint32_t og, ou;
+    swiglu_bwd_pair(h[row * F + c], h[row * F + f2 + c], da[i], og, ou);
     dh[row * F + c] = og;
     dh[row * F + f2 + c] = ou;
   }
@@ -788,6 +815,90 @@ __global__ __launch_bounds__(kColThreads) void quant_row_requant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// SwiGLU backward fused with the row-wise quantize + column-wise requantize
+// of its output
+// ---------------------------------------------------------------------------
+
+// h [T, 2F] and da [T, F] bf16 -> what swiglu_bwd_kernel followed by
+// quant_row_requant_kernel on dh [T, 2F] writes (row-wise codes and scales,
+// the column-wise copy requantized from them, the dbias partials), without
+// writing dh.  Tile (t0, c0) of the F columns gives two 128 x 128 tiles of
+// dh, the gate part at columns c0.. and the up part at F + c0..: each chunk
+// of gate, up and da becomes a chunk of each part, quantized row-wise from
+// registers and staged in that part's LDS buffer, and requant_tile_fast then
+// runs on both buffers unchanged, so every byte and partial sum is that of
+// the two-kernel path (bf16 row scale bytes are at most kMaxFastScaleByte).
+// Four resident workgroups per CU keep the reads in flight.
+// The tile's loads are issued half at a time (gate, up and da for 4 of the 8
+// chunks per thread, then the other 4): 109 VGPRs, so four workgroups fit on
+// a CU (the LDS allows four).  All 8 at once took 149 VGPRs and three
+// workgroups and was 7 % slower; quarters (86 VGPRs) 1 % slower.
+constexpr int kSwigluBwdHalves = 2;
+constexpr int kSwigluBwdWgPerCu = 4;
+template <bool kDbias>
+__global__ __launch_bounds__(kColThreads) void swiglu_bwd_quant_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ da, int64_t T, int64_t F,
+    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col,
+    uint8_t* __restrict__ s_col, float* __restrict__ partial, int32_t ntf, int32_t ntiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kLdsBytesU8];
+  __shared__ float lds_sc[2][kLdsScWords];           // row scales as conversion operands
+  const int tid = threadIdx.x;
+  const int64_t K = 2 * F;                           // dh columns
+  for (int tile = blockIdx.x; tile < ntiles; tile += (int)gridDim.x) {
+    int64_t c0, t0;
+    tile_origin(tile, ntf, c0, t0);
+    // chunk jj of this thread: row 16 jj + tid / 16, its 8 elements
+    // 8 (tid % 16) .. + 7; the quad of lanes 4b..4b+3 holds block b
+    const uint32_t oh = opaque_u32((uint32_t)(tid >> 4) * (uint32_t)K + (tid & 15) * 8);
+    const uint32_t od = opaque_u32((uint32_t)(tid >> 4) * (uint32_t)F + (tid & 15) * 8);
+#pragma unroll
+    for (int hh = 0; hh < kSwigluBwdHalves; ++hh) {
+      constexpr int kN = 8 / kSwigluBwdHalves;
+      u32x4 gv[kN], uv[kN], dv[kN];
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int jj = kN * hh + i;
+        const uint16_t* hb = h + (t0 + 16 * jj) * K + c0;   // uniform
+        gv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hb + oh));
+        uv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(hb + F + oh));
+        dv[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(da + (t0 + 16 * jj) * F + c0 + od));
+      }
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int jj = kN * hh + i;
+        const int idx = tid + kColThreads * jj;
+        const int r = idx >> 4, cc = idx & 15;
+        uint4 cg, cu;
+        swiglu_bwd_pair(gv[i].x, uv[i].x, dv[i].x, cg.x, cu.x);
+        swiglu_bwd_pair(gv[i].y, uv[i].y, dv[i].y, cg.y, cu.y);
+        swiglu_bwd_pair(gv[i].z, uv[i].z, dv[i].z, cg.z, cu.z);
+        swiglu_bwd_pair(gv[i].w, uv[i].w, dv[i].w, cg.w, cu.w);
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const uint4 c = part ? cu : cg;
+          const uint32_t amax = quad_max(chunk_amax_bits(c));
+          const uint32_t byte = scale_byte_from_exp(amax >> 7);
+          const int64_t rb = t0 * K + c0 + part * F + 16 * jj * K;   // uniform
+          const uint2 e = encode_chunk(c, byte);
+          *reinterpret_cast<uint2*>(q_row + rb + oh) = e;
+          *reinterpret_cast<uint2*>(&lds[part][lds_off_u8(r, cc * 8)]) = e;
+          if ((cc & 3) == 0) lds_sc[part][lds_sc_idx(r, cc >> 2)] = e8m0_operand(byte);
+          const uint32_t bytes4 = gather_blocks4(byte);
+          if ((tid & 15) == 0)
+            *reinterpret_cast<uint32_t*>(s_row + (rb >> 5) + (oh >> 5)) = bytes4;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one half's loads at a time
+    }
+    __syncthreads();
+    requant_tile_fast<kDbias>(lds[0], lds_sc[0], T, K, c0, t0, q_col, s_col, partial);
+    requant_tile_fast<kDbias>(lds[1], lds_sc[1], T, K, F + c0, t0, q_col, s_col, partial);
+    __syncthreads();   // every LDS read of this tile is done before the next write
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -863,6 +974,21 @@ hipError_t launch_quant_row_requant(const uint16_t* x, int64_t T, int64_t K, uin
   return hipGetLastError();
 }
 
+hipError_t launch_swiglu_bwd_quant(const uint16_t* h, const uint16_t* da, int64_t T, int64_t F,
+                                   uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                   float* partial, hipStream_t st) {
+  const int32_t ntt = (int32_t)(T / kTileT), ntf = (int32_t)(F / kTileK);
+  const int32_t ntiles = ntt * ntf;
+  const int grid = (int)std::min<int64_t>(ntiles, (int64_t)device_cus() * kSwigluBwdWgPerCu);
+  if (partial != nullptr)
+    hipLaunchKernelGGL(swiglu_bwd_quant_kernel<true>, dim3(grid), dim3(kColThreads), 0, st, h, da,
+                       T, F, q_row, s_row, q_col, s_col, partial, ntf, ntiles);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_quant_kernel<false>, dim3(grid), dim3(kColThreads), 0, st, h,
+                       da, T, F, q_row, s_row, q_col, s_col, partial, ntf, ntiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_dbias_partial(const uint8_t* q_row, const uint8_t* s_row, int64_t T, int64_t N,
                                 float* partial, hipStream_t st) {
   dim3 grid((unsigned)(N / 256), (unsigned)(T / kTileT));
@@ -909,7 +1035,7 @@ size_t scaled_bias_workspace_bytes(int64_t T, int64_t N) {
 
 hipError_t launch_dbias_finalize(const float* partial, const int64_t* m_splits, int32_t G,
                                  int64_t T, int64_t K, float* dbias, hipStream_t st) {
-  dim3 grid((unsigned)G, (unsigned)((K + 255) / 256));
+  dim3 grid((unsigned)G, (unsigned)((K + 63) / 64));
   hipLaunchKernelGGL(dbias_finalize_kernel, grid, dim3(256), 0, st, partial, m_splits, G, T, K,
                      dbias);
   return hipGetLastError();

@@ -53,7 +53,7 @@ def test_no_tokens_anywhere():
     main = torch.full((g, n, k), 2.5, device="cuda")
     mx.grouped_gemm_wgrad_accumulate(e(n, 0), e(n, 0), e(k, 0), e(k, 0), ms, 0, n, k, main)
     db = mx.grouped_dbias(e(0, n), e(0, n // 32), ms, dbias=torch.full((g, n), 9.0, device="cuda"))
-    log("edges: T = 0 quantize, requant with dbias, SwiGLU")
+    log("edges: T = 0 quantize, requant with dbias, SwiGLU, SwiGLU backward + quantize")
     bf = torch.bfloat16
     xo = mx.group_quantize(torch.zeros(0, k, dtype=bf, device="cuda"), mx.ROWWISE | mx.COLWISE)
     _, db2 = mx.requant_colwise(xo.row_data, xo.row_scale, ms, with_dbias=True,
@@ -62,12 +62,15 @@ def test_no_tokens_anywhere():
     ao = mx.swiglu_quantize(h)
     a = mx.swiglu_fwd(h)
     dh = mx.swiglu_bwd(h, a)
+    bq, db3 = mx.swiglu_bwd_quantize(h, a, ms, with_dbias=True,
+                                     dbias=torch.full((g, 2 * n), 6.0, device="cuda"))
     torch.cuda.synchronize()
     assert torch.count_nonzero(dw).item() == 0
     assert torch.all(main == 2.5)
     assert torch.count_nonzero(db).item() == 0
     assert torch.count_nonzero(db2).item() == 0
     assert xo.col_data.shape == (k, 0) and ao.row_data.shape == (0, n) and dh.shape == (0, 2 * n)
+    assert torch.count_nonzero(db3).item() == 0 and bq.col_data.shape == (2 * n, 0)
 
 
 @pytest.mark.parametrize("seed", [0, 1])

@@ -393,3 +393,40 @@ def test_fullsize_fused_mlp_fc2_and_swiglu():
     for gi, m in enumerate(splits):
         if m == 0:
             assert torch.count_nonzero(dw2[gi]).item() == 0, f"expert {gi} has no tokens"
+
+
+def test_fullsize_swiglu_bwd_quantize():
+    """The fused SwiGLU backward + quantize + requantize (+ dbias) at the fused
+    MLP's full size (83968 tokens, F = 1024, 64 Zipf-routed experts), the
+    launch bench.py times: every byte and the dbias bits against swiglu_bwd
+    followed by group_quantize_requant, and sampled rows and 128-token column
+    blocks against the oracle's quantize of the GPU's dh."""
+    name = "nemotron_proxy_mlp"
+    splits = [int(v) for v in wl.splits_for(name)]
+    t, f = sum(splits), wl.make(name, parts=set()).ffn // 2
+    rng = np.random.default_rng(26)
+    gen = torch.Generator(device="cuda").manual_seed(26)
+    bf = torch.bfloat16
+    log(f"full-size {name}: SwiGLU backward + quantize, {t} x {2 * f}")
+    h = (torch.randn(t, 2 * f, device="cuda", generator=gen) * 3).to(bf)
+    da = torch.randn(t, f, device="cuda", generator=gen).to(bf)
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    dh = mx.swiglu_bwd(h, da)
+    ref, refdb = mx.group_quantize_requant(dh, ms, with_dbias=True)
+    got, db = mx.swiglu_bwd_quantize(h, da, ms, with_dbias=True)
+    torch.cuda.synchronize()
+    for a, b in ((got.row_data, ref.row_data), (got.row_scale, ref.row_scale),
+                 (got.col_data, ref.col_data), (got.col_scale, ref.col_scale)):
+        assert torch.equal(a, b)
+    assert torch.equal(db.view(torch.uint8), refdb.view(torch.uint8))
+    del ref, refdb
+    rows = torch.from_numpy(np.sort(rng.choice(t, size=256, replace=False))).cuda()
+    q, s = om.quantize_rowwise(f64(dh[rows]))
+    assert np.array_equal(u8(got.row_data[rows]), q) and np.array_equal(u8(got.row_scale[rows]), s)
+    for b in np.sort(rng.choice(t // 128, size=2, replace=False)):
+        # a 128-token block lies inside one expert (experts are multiples of 128)
+        blk = f64(dh[b * 128:(b + 1) * 128])
+        q, s = om.quantize_rowwise(blk)
+        cq, cs = om.requant_colwise(q, s, [128])
+        assert np.array_equal(u8(got.col_data[:, b * 128:(b + 1) * 128]), cq)
+        assert np.array_equal(u8(got.col_scale[:, 4 * b:4 * b + 4]), cs)

@@ -414,3 +414,68 @@ def test_quantize_requant_workloads(name):
     w = wl.make(name)
     _quantize_requant_case(w.tensors["dy"], [int(v) for v in w.m_splits], True)
     _quantize_requant_case(w.tensors["x"], [int(v) for v in w.m_splits], False)
+
+
+def _swiglu_bwd_case(t, f, seed, splits, with_dbias):
+    """mxfp8_swiglu_bwd_quantize against the two calls it replaces (every byte,
+    and dbias bit for bit), and its quantize part against the oracle applied
+    to the device's dh (which test_swiglu pins to within a bf16 ulp of the
+    oracle's SwiGLU backward)."""
+    h_cpu = _swiglu_input(t, f, seed)
+    rng = np.random.default_rng(seed + 1000)
+    da_cpu = torch.from_numpy(rng.standard_normal((t, f)).astype(np.float32)).to(torch.bfloat16)
+    h, da = h_cpu.to("cuda"), da_cpu.to("cuda")
+    ms = dev(np.asarray(splits, dtype=np.int64))
+    dh = mx.swiglu_bwd(h, da)
+    if with_dbias:
+        ref, refdb = mx.group_quantize_requant(dh, ms, with_dbias=True)
+        got, db = mx.swiglu_bwd_quantize(h, da, ms, with_dbias=True)
+    else:
+        ref = mx.group_quantize_requant(dh)
+        got = mx.swiglu_bwd_quantize(h, da)
+    torch.cuda.synchronize()
+    for a, b in zip(_mx_bytes(got), _mx_bytes(ref)):
+        assert np.array_equal(a, b)
+    if with_dbias:
+        assert torch.equal(db.view(torch.uint8), refdb.view(torch.uint8))
+    dh64 = f64(dh)
+    assert og.within_bf16_ulp(dh64, osw.swiglu_bwd(f64(h_cpu), f64(da_cpu))).all()
+    q, s = om.quantize_rowwise(dh64)
+    cq, cs = om.requant_colwise(q, s, splits)
+    assert np.array_equal(u8(got.row_data), q) and np.array_equal(u8(got.row_scale), s)
+    assert np.array_equal(u8(got.col_data), cq) and np.array_equal(u8(got.col_scale), cs)
+    if with_dbias:
+        ref_db = om.grouped_dbias(q, s, splits)
+        absx = np.abs(om.dequantize_rowwise(q, s))
+        bound = np.zeros_like(ref_db)
+        start = 0
+        for g, m in enumerate(splits):
+            bound[g] = absx[start:start + m].sum(axis=0)
+            start += m
+        assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - ref_db) <= 1e-5 * bound + 1e-6)
+
+
+@pytest.mark.parametrize("t,f,seed,splits", [
+    (256, 256, 41, [256]),
+    (384, 512, 42, [128, 0, 256]),
+    (1024, 1536, 43, [384, 128, 0, 512]),
+])
+@pytest.mark.parametrize("with_dbias", [False, True])
+def test_swiglu_bwd_quantize(t, f, seed, splits, with_dbias):
+    log(f"swiglu_bwd_quantize {t}x{f} splits {splits} dbias {with_dbias}")
+    _swiglu_bwd_case(t, f, seed, splits, with_dbias)
+
+
+def test_swiglu_bwd_quantize_reuses_outputs():
+    log("swiglu_bwd_quantize reuses outputs")
+    t, f = 256, 512
+    h1, h2 = _swiglu_input(t, f, 51).to("cuda"), _swiglu_input(t, f, 52).to("cuda")
+    da = torch.ones(t, f, dtype=torch.bfloat16, device="cuda")
+    out = mx.swiglu_bwd_quantize(h1, da)
+    ptrs = (out.row_data.data_ptr(), out.col_data.data_ptr())
+    out = mx.swiglu_bwd_quantize(h2, da, out=out)
+    ref = mx.group_quantize_requant(mx.swiglu_bwd(h2, da))
+    torch.cuda.synchronize()
+    assert (out.row_data.data_ptr(), out.col_data.data_ptr()) == ptrs
+    for a, b in zip(_mx_bytes(out), _mx_bytes(ref)):
+        assert np.array_equal(a, b)

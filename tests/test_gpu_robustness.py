@@ -87,15 +87,28 @@ def _run_all(w, x, wt, dy, h, g):
     a = mx.swiglu_fwd(h, out=g((t, f), bf))
     dh = mx.swiglu_bwd(h, a, out=g((t, 2 * f), bf))
     ao = mx.swiglu_quantize(h, out=_mx(g, t, f))
+    # the SwiGLU backward fused with the quantize of dh (dbias and workspace guarded)
+    dhq, dbh = mx.swiglu_bwd_quantize(
+        h, a, ms, with_dbias=True, out=_mx(g, t, 2 * f), dbias=g((G, 2 * f), f32),
+        workspace=g((mx.dbias_workspace_bytes(t, 2 * f),), torch.uint8))
+    # FC1 (W as [G, 2F', K] with F' = n / 2) with the SwiGLU + quantize
+    # epilogue, where F' meets its 512 alignment
+    hs = a2 = None
+    if (n // 2) % 512 == 0:
+        hs, a2 = mx.grouped_gemm_swiglu_quantize(xo.row_data, xo.row_scale, wo.row_data,
+                                                 wo.row_scale, ms, t, n // 2, k, h=g((t, n), bf),
+                                                 out=_mx(g, t, n // 2))
     torch.cuda.synchronize()
     for name, v in (("xo", xo), ("wo", wo), ("dyo", dyo), ("xc", xc), ("dyc", dyc), ("ao", ao),
-                    ("xf", xf), ("dyf", dyf)):
+                    ("xf", xf), ("dyf", dyf), ("dhq", dhq), ("a2", a2)):
         for part in ("row_data", "row_scale", "col_data", "col_scale"):
-            if getattr(v, part) is not None:
+            if v is not None and getattr(v, part) is not None:
                 out[f"{name}.{part}"] = getattr(v, part).clone()
     for name, v in (("db", db), ("db2", db2), ("dbf", dbf), ("sdb", sdb), ("sds", sds), ("y", y),
-                    ("dx", dx), ("dw", dw), ("dw2", dw2), ("mg", mg), ("a", a), ("dh", dh)):
-        out[name] = v.clone()
+                    ("dx", dx), ("dw", dw), ("dw2", dw2), ("mg", mg), ("a", a), ("dh", dh),
+                    ("dbh", dbh), ("hs", hs)):
+        if v is not None:
+            out[name] = v.clone()
     return out
 
 

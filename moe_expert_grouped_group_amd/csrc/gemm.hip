@@ -1114,10 +1114,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       }
     }
     // wgrad accumulating into C (fp32): an expert without tokens (nk == 0)
-    // leaves its C untouched, and the old values are loaded 16 at a time
-    // (one 4-row block of every fragment) before they are added: the wait
-    // for a load also waits for every store issued before it, so loading one
-    // value at a time would serialise.  Registers 4b..4b+3 of a quad of
+    // leaves its C untouched, and the old values are loaded a block of 16
+    // rows ahead of the stores: the wait for a load also waits for every
+    // store issued before it (the counter completes in issue order), so
+    // loading just before adding would serialise.  Registers 4b..4b+3 of a quad of
     // lanes (4 consecutive columns) hold a 4 x 4 block of C; a DPP transpose
     // inside the quad leaves lane q of it with row 8b + 4 (l/32) + q, its 4
     // columns in registers 0..3, so one 16-byte load and store per 4
@@ -1142,20 +1142,32 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       const uint32_t lane_off =
           my_row * (uint32_t)ldc_b + (uint32_t)(wn * WT) * (uint32_t)esz + 4 * cq * (uint32_t)esz;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
+      // Eight blocks h of 16 rows (two 8-row groups of 32-row fragment
+      // row h / 2): the old values of block h + 1 are loaded before block h
+      // is stored, so the wait for block h + 1's loads leaves block h's
+      // stores in flight.  Two blocks of old values are live (64 registers).
+      f32x4 old[2][2][4];
+      auto load_block = [&](int h, f32x4 (&o)[2][4]) {
+        const int i = h >> 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 old[4][4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int row = wm_u * WT + 32 * i + 8 * b;
+        for (int bb = 0; bb < 2; ++bb) {
+          const int row = wm_u * WT + 32 * i + 8 * (2 * (h & 1) + bb);
           const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            old[b][j] = __builtin_nontemporal_load(
+            o[bb][j] = __builtin_nontemporal_load(
                 (__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4));
         }
+      };
+      load_block(0, old[0]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+      for (int h = 0; h < 8; ++h) {
+        if (h + 1 < 8) load_block(h + 1, old[(h + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = h >> 1;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b = 2 * (h & 1) + bb;
           const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
           char* rbase = (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
@@ -1163,14 +1175,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
             float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
             float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
             quad_transpose(v0, v1, v2, v3, odd, hi2);
-            v0 += old[b][j].x;
-            v1 += old[b][j].y;
-            v2 += old[b][j].z;
-            v3 += old[b][j].w;
+            const f32x4 ov = old[h & 1][bb][j];
+            v0 += ov.x;
+            v1 += ov.y;
+            v2 += ov.z;
+            v3 += ov.w;
             __builtin_nontemporal_store(f32x4{v0, v1, v2, v3},
                 (__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4));
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (!has_next) break;

@@ -1114,10 +1114,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       }
     }
     // wgrad accumulating into C (fp32): an expert without tokens (nk == 0)
-    // leaves its C untouched, and the old values are loaded a block of 16
+    // leaves its C untouched, and the old values are loaded a block of 8
     // rows ahead of the stores: the wait for a load also waits for every
     // store issued before it (the counter completes in issue order), so
-    // loading just before adding would serialise.  Registers 4b..4b+3 of a quad of
+    // loading just before adding would serialise.  (Blocks of 16 rows held
+    // 32 registers more and pushed the tile counter's claim into scratch,
+    // whose spill and reload each waited for every memory operation in
+    // flight.)  Registers 4b..4b+3 of a quad of
     // lanes (4 consecutive columns) hold a 4 x 4 block of C; a DPP transpose
     // inside the quad leaves lane q of it with row 8b + 4 (l/32) + q, its 4
     // columns in registers 0..3, so one 16-byte load and store per 4
@@ -1142,47 +1145,39 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
       const uint32_t lane_off =
           my_row * (uint32_t)ldc_b + (uint32_t)(wn * WT) * (uint32_t)esz + 4 * cq * (uint32_t)esz;
       typedef float f32x4 __attribute__((ext_vector_type(4)));
-      // Eight blocks h of 16 rows (two 8-row groups of 32-row fragment
-      // row h / 2): the old values of block h + 1 are loaded before block h
-      // is stored, so the wait for block h + 1's loads leaves block h's
-      // stores in flight.  Two blocks of old values are live (64 registers).
-      f32x4 old[2][2][4];
-      auto load_block = [&](int h, f32x4 (&o)[2][4]) {
-        const int i = h >> 1;
+      // Sixteen blocks h of 8 rows (8-row group h % 4 of 32-row fragment row
+      // h / 4): the old values of block h + 1 are loaded before block h is
+      // stored, so the wait for block h + 1's loads leaves block h's stores
+      // in flight.  Two blocks of old values are live (32 registers).
+      f32x4 old[2][4];
+      auto load_block = [&](int h, f32x4 (&o)[4]) {
+        const int row = wm_u * WT + 32 * (h >> 2) + 8 * (h & 3);
+        const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const int row = wm_u * WT + 32 * i + 8 * (2 * (h & 1) + bb);
-          const char* rb = (const char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            o[bb][j] = __builtin_nontemporal_load(
-                (__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4));
-        }
+        for (int j = 0; j < 4; ++j)
+          o[j] = __builtin_nontemporal_load(
+              (__attribute__((address_space(1))) const f32x4*)(rb + j * 32 * 4));
       };
       load_block(0, old[0]);
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        if (h + 1 < 8) load_block(h + 1, old[(h + 1) & 1]);
+      for (int h = 0; h < 16; ++h) {
+        if (h + 1 < 16) load_block(h + 1, old[(h + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        const int i = h >> 1;
+        const int i = h >> 2, b = h & 3;
+        const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
+        char* rbase = (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const int b = 2 * (h & 1) + bb;
-          const int row = wm_u * WT + 32 * i + 8 * b;   // uniform
-          char* rbase = (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
-            float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
-            quad_transpose(v0, v1, v2, v3, odd, hi2);
-            const f32x4 ov = old[h & 1][bb][j];
-            v0 += ov.x;
-            v1 += ov.y;
-            v2 += ov.z;
-            v3 += ov.w;
-            __builtin_nontemporal_store(f32x4{v0, v1, v2, v3},
-                (__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4));
-          }
+        for (int j = 0; j < 4; ++j) {
+          float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
+          float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
+          quad_transpose(v0, v1, v2, v3, odd, hi2);
+          const f32x4 ov = old[h & 1][j];
+          v0 += ov.x;
+          v1 += ov.y;
+          v2 += ov.z;
+          v3 += ov.w;
+          __builtin_nontemporal_store(f32x4{v0, v1, v2, v3},
+              (__attribute__((address_space(1))) f32x4*)(rbase + j * 32 * 4));
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -969,28 +969,63 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         // all stored unless it is a tail tile, part); the check is uniform:
         // rows R and R + 4 of one store lie in one 8-row group, and row_lo
         // and row_hi are multiples of 128
+        // bf16 with the SwiGLU epilogue: registers r and r + 1 (rows R and
+        // R + 1 of one column) are converted together, as the SwiGLU below
+        // converts them (the compiler shares the conversions), and lanes l
+        // and l ^ 1 (neighbouring columns) swap the pair: the even lane keeps
+        // row R of columns n, n + 1, the odd lane row R + 1 of columns n - 1,
+        // n, so one 32-bit store per two registers writes four 64-byte row
+        // pieces (FC1 + SwiGLU 9 % faster).  Other bf16 outputs keep two
+        // 2-byte stores per conversion: the same row pieces per instruction
+        // count, and there the swap's extra VALU cost 2-7 %.
+        const bool odd_l = (ln & 1) != 0;
+        const uint32_t bsel = odd_l ? 0x03020706u : 0x05040100u;
+        const uint32_t lane_off_b = lane_off + (odd_l ? (uint32_t)ldc_b - 2u : 0u);
         auto store_rows = [&](auto check) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            if (OUT_BF16 && SWIGLU) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
-              if (decltype(check)::value && (row < lo || row >= hi)) continue;
-              char* rbase =
-                  (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
-              if (OUT_BF16) {
+              for (int r = 0; r < 16; r += 2) {
+                const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+                if (decltype(check)::value && (row < lo || row >= hi)) continue;
+                char* rbase =
+                    (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off_b;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+                  const uint32_t sw = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, true);
+                  const int64_t jo = j >= 2 ? 2 * p.f + (j - 2) * 64 : j * 64;
+                  __builtin_nontemporal_store(
+                      __builtin_amdgcn_perm(sw, pk, bsel),
+                      (__attribute__((address_space(1))) uint32_t*)(rbase + jo));
+                }
+              }
+            } else if (OUT_BF16) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+                if (decltype(check)::value && (row < lo || row >= hi)) continue;
+                char* rbase =
+                    (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
                 // two columns 32 apart per conversion (one V_CVT_PK_BF16_F32)
 #pragma unroll
                 for (int j = 0; j < 4; j += 2) {
                   const uint32_t pk = pack_bf16x2(acc[i][j][r], acc[i][j + 1][r]);
-                  const int64_t jo = SWIGLU && j == 2 ? 2 * p.f : j * 64;
                   __builtin_nontemporal_store(
-                      (uint16_t)pk, (__attribute__((address_space(1))) uint16_t*)(rbase + jo));
+                      (uint16_t)pk, (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64));
                   __builtin_nontemporal_store(
                       (uint16_t)(pk >> 16),
-                      (__attribute__((address_space(1))) uint16_t*)(rbase + jo + 64));
+                      (__attribute__((address_space(1))) uint16_t*)(rbase + j * 64 + 64));
                 }
-              } else {
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = wm_u * WT + 32 * i + 8 * (r / 4) + (r % 4);
+                if (decltype(check)::value && (row < lo || row >= hi)) continue;
+                char* rbase =
+                    (char*)uniform_ptr((const uint8_t*)(ed.c + (int64_t)row * ldc_b)) + lane_off;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                   __builtin_nontemporal_store(

@@ -372,14 +372,14 @@ __device__ __forceinline__ TileDesc describe(const GemmArgs& p, const ExpertTabl
     const int g = t->order[pos / per_expert];
     const int rem = pos % per_expert;
     int mtl = rem / p.ntiles_n, nt = rem % p.ntiles_n;
-    // Blocked dynamic order (dynamic == 2, the accumulating wgrad): XCD x
-    // takes the positions congruent to x mod 8 (one counter per XCD).  Where
-    // the tile grid splits into 4 x 2 blocks, those positions of an expert
-    // map onto block x (a quarter of the row panels, half the column panels)
-    // instead of two whole tile columns, so each dY panel is read by two XCDs
-    // rather than all eight: accumulating wgrad 1.60 -> 1.53 ms; the plain
-    // wgrad, which only writes its output, was 7 % slower this way.  A
-    // bijection of the expert's tiles either way.
+    // Blocked dynamic order (dynamic == 2: the accumulating wgrad and the
+    // bf16 wgrad): XCD x takes the positions congruent to x mod 8 (one
+    // counter per XCD).  Where the tile grid splits into 4 x 2 blocks, those
+    // positions of an expert map onto block x (a quarter of the row panels,
+    // half the column panels) instead of two whole tile columns, so each dY
+    // panel is read by two XCDs rather than all eight: accumulating wgrad
+    // 1.60 -> 1.53 ms; the fp32 wgrad, whose output writes dominate, was 7 %
+    // slower this way.  A bijection of the expert's tiles either way.
     if (dynamic == 2 && (p.band & 3) == 0 && (p.ntiles_n & 1) == 0) {
       const int x = rem & 7, k = rem >> 3;
       const int rows = p.band >> 2, cols = p.ntiles_n >> 1;
@@ -670,7 +670,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
   };
 
   UnitPlan up = plan_units<KGROUPED>(p, &table, ntiles, (int)gridDim.x);
-  if (ACCUM && up.dynamic) up.dynamic = 2;   // blocked order (describe)
+  // blocked order (describe): the accumulating wgrad, and the bf16 wgrad
+  // (fused MLP, 64 experts: FC2 wgrad 0.401 -> 0.389 ms, FC1 0.602 -> 0.592)
+  if ((ACCUM || (KGROUPED && OUT_BF16)) && up.dynamic) up.dynamic = 2;
   int tile = blockIdx.x;   // unit index (a tile, or half of one: describe_unit)
   if (tile >= up.nunits) return;
   // Dynamic order (wgrad with a tile counter): the next tile must be known

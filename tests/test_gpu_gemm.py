@@ -150,7 +150,7 @@ def test_split_contraction_halves(kind, layout):
 # few long tiles beside many short ones), one empty expert, so the tiles go
 # through the counter; at N = K = 512 that is 96 tiles (fewer than the CUs),
 # at N = K = 2048 1536 tiles, several per workgroup, with 4 x 2 tile blocks
-# per expert (the accumulating wgrad's blocked order); then 8 experts, none
+# per expert (the blocked order of the accumulating and bf16 wgrads); then 8 experts, none
 # empty, 1024 tiles.
 COUNTER_CASES = [
     ([0, 3072, 128, 256, 128] + [128] * 19, 1024, 512),
@@ -166,8 +166,8 @@ def test_wgrad_tile_counter_same_bytes(case):
     fp32 and bf16 and accumulated into main_grad, twice with one workspace.
     The COUNTER_CASES have fewer than 1 in 8 experts empty, so their tiles go
     through the counter (the last two with several tiles per workgroup: the
-    counter's hand-out past the first round, and the accumulating wgrad's
-    blocked order); the CASES (1 in 4 or more empty, or a single expert)
+    counter's hand-out past the first round, and the blocked order of the
+    bf16 and accumulating wgrads); the CASES (1 in 4 or more empty, or a single expert)
     cover the kernel's choice of the fixed order despite a workspace."""
     if case < len(CASES):
         splits, n, k = CASES[case]

@@ -977,9 +977,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
         // and l ^ 1 (neighbouring columns) swap the pair: the even lane keeps
         // row R of columns n, n + 1, the odd lane row R + 1 of columns n - 1,
         // n, so one 32-bit store per two registers writes four 64-byte row
-        // pieces (FC1 + SwiGLU 9 % faster).  Other bf16 outputs keep two
-        // 2-byte stores per conversion: the same row pieces per instruction
-        // count, and there the swap's extra VALU cost 2-7 %.
+        // pieces (FC1 + SwiGLU 5 % faster).  Other bf16 outputs keep two
+        // 2-byte stores per conversion: they write as many 64-byte pieces in
+        // all, and there the swap's extra VALU cost 2-7 % (so did a swap that
+        // makes each store a whole 128-byte line per row: 0 to +4 %).
         const bool odd_l = (ln & 1) != 0;
         const uint32_t bsel = odd_l ? 0x03020706u : 0x05040100u;
         const uint32_t lane_off_b = lane_off + (odd_l ? (uint32_t)ldc_b - 2u : 0u);

@@ -272,7 +272,7 @@ def vendor_reference(m, n, k, steps):
     GEMM with the flops of one grouped launch of the headline workload
     (M = all tokens, N, K): MXFP8 with E8M0 block scales, and FP8 with one
     scale per tensor.  Context for the grouped kernel's rate, not part of
-    the path; an entry holds the error text where this build lacks a form."""
+    the path; an entry holds the error text where the installed torch lacks a form."""
     import torch
     dev = "cuda"
     gen = torch.Generator(device=dev)

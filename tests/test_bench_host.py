@@ -75,6 +75,34 @@ def _pmc_dir(tmp, sub, launches):
     return d
 
 
+def test_summarize_trace(tmp_path):
+    """Per-label calls, mean / median / min / max and share from a
+    --kernel-trace CSV: the M-grouped GEMM alternates forward and dgrad in
+    dispatch order, and a kernel launched for several purposes takes the
+    names it is given in turn."""
+    d = os.path.join(str(tmp_path), "trace")
+    os.makedirs(d)
+    fw, kg = _name(False, False, sw=False), _name(True, False, sw=False)
+    rc = "void mx::quant_rowcol_kernel(unsigned short const*, long)"
+    launches = [(rc, 40000), (rc, 20000), (fw, 100000), (fw, 200000), (kg, 300000),
+                (rc, 44000), (rc, 22000), (fw, 110000), (fw, 210000), (kg, 310000)]
+    with open(os.path.join(d, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t0 = 5000
+        for name, dur in launches:
+            w.writerow(["KERNEL_DISPATCH", name, t0, t0 + dur])
+            t0 += dur + 100
+    md = bench.summarize_trace(d, "t", ["cmd"],
+                               cycles={"quant_rowcol_kernel": ["quant_w1", "quant_w2"]})
+    total = sum(dur for _, dur in launches) / 1e3
+    assert f"| `wgrad_TN` | 2 | 305.0 | 310.0 | 300.0 | 310.0 | 0.610 | {100 * 610 / total:.1f} |" in md
+    assert "| `dgrad_NN` | 2 | 205.0 |" in md and "| `forward_NT` | 2 | 105.0 |" in md
+    assert "| `quant_w1` | 2 | 42.0 |" in md and "| `quant_w2` | 2 | 21.0 |" in md
+    # rows by total time, longest first
+    assert md.index("| `wgrad_TN`") < md.index("| `dgrad_NN`") < md.index("| `forward_NT`")
+
+
 def test_summarize_mfma(tmp_path):
     fw, dg = _name(False, False, sw=False), _name(False, False, sw=False)
     # 100 us at 2 GHz: 200000 active cycles per XCD; MFMA busy half the
